@@ -1,0 +1,166 @@
+/*
+ * lora_mi355x.h -- C ABI of the segmented-gather multi-LoRA library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow three vLLM API documentation pages:
+ *   - "lora_kernel_metadata": class LoRAKernelMeta (make, _reset,
+ *     prepare_tensors, meta_args);
+ *   - "punica_gpu": class PunicaWrapperGPU (add_shrink, add_expand,
+ *     add_lora_linear);
+ *   - "punica_tpu": class PunicaWrapperTPU (add_expand's running column
+ *     offset, _apply_bias).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers unless marked "host".
+ *   - Every call is asynchronous on `stream` (NULL = the null stream); none
+ *     allocates memory, synchronizes the device, or keeps state between calls,
+ *     so prepare + shrink + expand on fixed buffers can be captured in a HIP
+ *     graph.  Calls that overlap on the same buffers race.
+ *   - The caller owns every buffer.
+ *   - Return value: LORA_OK (0) or a negative lora_status_t, decided on the
+ *     host before anything is launched (nothing is launched on error), or
+ *     LORA_ERR_LAUNCH if the HIP runtime refused a launch.
+ *   - Element types: token ids and metadata int32; x, y, weights and bias
+ *     bfloat16 (raw 16-bit patterns); the shrink buffer float32.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_NULL = -1,          /* a required pointer is NULL */
+    LORA_ERR_NUM_TOKENS = -2,    /* N < 0, N > max_num_tokens, or N differs from the prepared N */
+    LORA_ERR_SHAPE = -3,         /* hidden / rank / slice widths / leading dims out of range */
+    LORA_ERR_MAX_LORAS = -4,     /* max_loras outside [1, LORA_MAX_LORAS] */
+    LORA_ERR_BUFFER = -5,        /* metadata region too small or misaligned */
+    LORA_ERR_ALIGN = -6,         /* a bf16 / fp32 operand is not 16-byte aligned as required */
+    LORA_ERR_SLICES = -7,        /* num_slices outside [1, LORA_MAX_SLICES] */
+    LORA_ERR_LAUNCH = -8,        /* the HIP runtime rejected a kernel launch or copy */
+    LORA_ERR_ID_RANGE = -9       /* device-side only: written to meta->status by prepare */
+} lora_status_t;
+
+#define LORA_MAX_LORAS 1023      /* ids 0 .. 1022; -1 = no LoRA */
+#define LORA_MAX_SLICES 8
+#define LORA_MAX_RANK 128
+
+/*
+ * Per-batch kernel metadata (LoRAKernelMeta on the "lora_kernel_metadata"
+ * page).  All arrays are views into ONE caller-owned device region bound by
+ * lora_meta_bind(); sizes are those make() gives:
+ *   token_lora_mapping     int32[max_num_tokens]  copy of the batch's ids
+ *   token_indices_sorted   int32[max_num_tokens]  token indices, stable-sorted by id
+ *   active_lora_ids        int32[max_loras + 1]   distinct ids present, ascending,
+ *                                                 -1 first when present; padding -1
+ *   num_tokens_per_lora    int32[max_loras + 1]   tokens per active id; padding 0
+ *   lora_token_start_loc   int32[max_loras + 2]   0, then running sums; padding 0
+ *   no_lora_flag           int32[1]   1 when every id is -1 (or N == 0)
+ *   status                 int32[1]   0, or LORA_ERR_ID_RANGE when some id was
+ *                                     outside [-1, max_loras) (such ids count as -1)
+ * The struct itself lives in host memory; lora_prepare_meta() records
+ * num_tokens in it.
+ */
+typedef struct lora_meta {
+    int32_t *token_lora_mapping;
+    int32_t *token_indices_sorted;
+    int32_t *active_lora_ids;
+    int32_t *num_tokens_per_lora;
+    int32_t *lora_token_start_loc;
+    int32_t *no_lora_flag;
+    int32_t *status;
+    int32_t *host_no_lora;   /* optional host pinned word (NULL = none): prepare copies
+                                no_lora_flag into it asynchronously on its stream */
+    int32_t max_loras;
+    int32_t max_num_tokens;
+    int32_t num_tokens;      /* set by lora_prepare_meta; -1 before the first prepare */
+} lora_meta_t;
+
+/* Bytes of device memory lora_meta_bind() needs for these maximum sizes
+ * (the allocation make() performs, as one region).  0 if the sizes are out
+ * of range. */
+size_t lora_meta_bytes(int max_loras, int max_num_tokens);
+
+/* Carve the metadata arrays out of `dev` (device pointer, 256-byte aligned,
+ * at least lora_meta_bytes() bytes) and fill `out` (host).  No device work
+ * is done: the arrays hold garbage until the first lora_prepare_meta().
+ * host_no_lora is set to NULL; the caller may point it at pinned host memory. */
+int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out);
+
+/*
+ * LoRAKernelMeta._reset + prepare_tensors for one batch
+ * ("lora_kernel_metadata" page).  mapping: int32[num_tokens] token -> LoRA id
+ * (-1 = none), device memory.  On device, in one launch:
+ *   reset active ids to -1, counts and start_loc to 0; set no_lora_flag to
+ *   all(mapping == -1); if set, stop there (mapping copy and sorted indices
+ *   are left as they were, as the pages' early return does); otherwise copy
+ *   the mapping, stable-sort token indices by id (ascending, ties in token
+ *   order), write the distinct ids with their counts, and the segment starts.
+ * Ids outside [-1, max_loras) are treated as -1 and reported in meta->status.
+ * The result is deterministic and bit-exact.  Records meta->num_tokens.
+ */
+int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta, hipStream_t stream);
+
+/*
+ * lora_shrink (PunicaWrapperGPU.add_shrink on the "punica_gpu" page; the
+ * fp32 buffer of add_lora_linear): for each slice i < num_slices and each
+ * token t whose id m is not -1,
+ *     buf[i][t][j] += scale * sum_k x[t][k] * lora_a[i][m][j][k]   (j < rank)
+ * accumulated in float32.  Rows of tokens with id -1 are not touched; when
+ * the no-LoRA flag is set nothing is touched.
+ *   x       bf16 [num_tokens][ldx], rows 16-byte aligned (ldx % 8 == 0)
+ *   lora_a  host array [num_slices] of device pointers, each bf16
+ *           [max_loras][rank][hidden] (hidden contiguous), 16-byte aligned
+ *   buf     float32 [num_slices][num_tokens][rank], 16-byte aligned
+ *   hidden % 8 == 0, rank % 8 == 0, 8 <= rank <= LORA_MAX_RANK
+ * num_tokens must equal the N of the last lora_prepare_meta() on `meta`,
+ * whose results must be complete in stream order.  Split-K partial sums are
+ * combined with float atomics, so the last bits may vary between runs.
+ */
+int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden,
+                const void *const *lora_a, int num_slices, int rank,
+                float *buf, const lora_meta_t *meta, float scale, hipStream_t stream);
+
+/*
+ * lora_expand with the per-slice bias folded in (PunicaWrapperGPU.add_expand
+ * on the "punica_gpu" page; the running offset of PunicaWrapperTPU.add_expand
+ * and the bias rule of PunicaWrapperTPU._apply_bias on the "punica_tpu"
+ * page): slice i covers columns [off_i, off_i + slice_widths[i]) of y with
+ * off_0 = offset_start and off_{i+1} = off_i + slice_widths[i]; for each token
+ * t whose id m is not -1 and each column c of slice i,
+ *     v = sum_j buf[i][t][j] * lora_b[i][m][c - off_i][j] (+ bias[i][m][c - off_i])
+ *     y[t][c] = bf16_rne((add_inputs ? y[t][c] : 0) + v)
+ * accumulated in float32 with a single rounding to bfloat16.  Rows of tokens
+ * with id -1 are not touched (no bias either); with the no-LoRA flag set
+ * nothing is touched.
+ *   buf          float32 [num_slices][num_tokens][rank], 16-byte aligned
+ *   lora_b       host array [num_slices] of device pointers, bf16
+ *                [max_loras][slice_widths[i]][rank] (rank contiguous)
+ *   bias         NULL, or host array [num_slices] of (NULL | device bf16
+ *                [max_loras][slice_widths[i]])
+ *   slice_widths host int[num_slices], each > 0 and % 8 == 0
+ *   y            bf16 [num_tokens][ldy], ldy % 8 == 0, offset_start % 8 == 0,
+ *                offset_start + sum(slice_widths) <= ldy
+ * num_tokens must equal the prepared N, as for lora_shrink.
+ */
+int lora_expand(const float *buf, int num_tokens, int rank,
+                const void *const *lora_b, const void *const *bias,
+                const int *slice_widths, int num_slices,
+                void *y, int64_t ldy, int offset_start, int add_inputs,
+                const lora_meta_t *meta, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *lora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,187 @@
+"""Python binding of liblora_mi355x.so (segmented-gather multi-LoRA on MI355X).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Torch tensors supply device memory and the current HIP stream.  The names
+mirror the C ABI in include/lora_mi355x.h:
+
+    lora_meta_bytes, lora_meta_bind, lora_prepare_meta, lora_shrink,
+    lora_expand, lora_status_string
+
+plus ``LoraMeta``, a holder that owns one device region sized by
+``lora_meta_bytes`` (LoRAKernelMeta.make on the "lora_kernel_metadata" page)
+and exposes its arrays as tensor views.
+
+Importing this package loads the library; it raises if the library has not
+been built (``python -m segmented_gather_lora_amd._build``): there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+from ._build import LIB as _LIB_PATH
+
+LORA_OK = 0
+LORA_ERR_NULL = -1
+LORA_ERR_NUM_TOKENS = -2
+LORA_ERR_SHAPE = -3
+LORA_ERR_MAX_LORAS = -4
+LORA_ERR_BUFFER = -5
+LORA_ERR_ALIGN = -6
+LORA_ERR_SLICES = -7
+LORA_ERR_LAUNCH = -8
+LORA_ERR_ID_RANGE = -9
+
+LORA_MAX_LORAS = 1023
+LORA_MAX_SLICES = 8
+LORA_MAX_RANK = 128
+
+EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
+            "lora_expand", "lora_status_string")
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, lora_status_string(status), status))
+
+
+class lora_meta_t(ctypes.Structure):
+    _fields_ = [
+        ("token_lora_mapping", ctypes.c_void_p),
+        ("token_indices_sorted", ctypes.c_void_p),
+        ("active_lora_ids", ctypes.c_void_p),
+        ("num_tokens_per_lora", ctypes.c_void_p),
+        ("lora_token_start_loc", ctypes.c_void_p),
+        ("no_lora_flag", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("host_no_lora", ctypes.c_void_p),
+        ("max_loras", ctypes.c_int32),
+        ("max_num_tokens", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("liblora_mi355x.so is not built (%s); run "
+                          "`python -m segmented_gather_lora_amd._build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.lora_meta_bytes.restype = ctypes.c_size_t
+    lib.lora_meta_bytes.argtypes = [i32, i32]
+    lib.lora_meta_bind.restype = i32
+    lib.lora_meta_bind.argtypes = [P, ctypes.c_size_t, i32, i32, ctypes.POINTER(lora_meta_t)]
+    lib.lora_prepare_meta.restype = i32
+    lib.lora_prepare_meta.argtypes = [P, i32, ctypes.POINTER(lora_meta_t), P]
+    lib.lora_shrink.restype = i32
+    lib.lora_shrink.argtypes = [P, i64, i32, i32, P, i32, i32, P, ctypes.POINTER(lora_meta_t),
+                                ctypes.c_float, P]
+    lib.lora_expand.restype = i32
+    lib.lora_expand.argtypes = [P, i32, i32, P, P, P, i32, P, i64, i32, i32,
+                                ctypes.POINTER(lora_meta_t), P]
+    lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_status_string.argtypes = [i32]
+    return lib
+
+
+lib = _load()
+
+
+def lora_status_string(status: int) -> str:
+    return lib.lora_status_string(int(status)).decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != LORA_OK:
+        raise LoraError(st, where)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr_array(tensors) -> ctypes.Array:
+    return (ctypes.c_void_p * len(tensors))(*[None if t is None else t.data_ptr() for t in tensors])
+
+
+def lora_meta_bytes(max_loras: int, max_num_tokens: int) -> int:
+    return int(lib.lora_meta_bytes(int(max_loras), int(max_num_tokens)))
+
+
+def lora_meta_bind(dev_ptr: int, nbytes: int, max_loras: int, max_num_tokens: int) -> lora_meta_t:
+    m = lora_meta_t()
+    _check(lib.lora_meta_bind(dev_ptr, nbytes, int(max_loras), int(max_num_tokens), ctypes.byref(m)),
+           "lora_meta_bind")
+    return m
+
+
+class LoraMeta:
+    """One device region holding a batch's kernel metadata (make() on the
+    "lora_kernel_metadata" page: allocated once at maximum sizes, reused)."""
+
+    def __init__(self, max_loras: int, max_num_tokens: int, device="cuda"):
+        import torch
+        nbytes = lora_meta_bytes(max_loras, max_num_tokens)
+        if nbytes == 0:
+            raise LoraError(LORA_ERR_MAX_LORAS, "lora_meta_bytes")
+        # torch's caching allocator returns 512-byte aligned blocks
+        self.region = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.struct = lora_meta_bind(self.region.data_ptr(), nbytes, max_loras, max_num_tokens)
+        self.max_loras, self.max_num_tokens = max_loras, max_num_tokens
+
+    def _view(self, field: str, n: int):
+        off = getattr(self.struct, field) - self.region.data_ptr()
+        return self.region[off:off + 4 * n].view(__import__("torch").int32)
+
+    @property
+    def num_tokens(self) -> int:
+        return self.struct.num_tokens
+
+    def views(self) -> dict:
+        """Tensor views of the metadata arrays (sizes as make() allocates)."""
+        L, T = self.max_loras, self.max_num_tokens
+        return dict(token_lora_mapping=self._view("token_lora_mapping", T),
+                    token_indices_sorted=self._view("token_indices_sorted", T),
+                    active_lora_ids=self._view("active_lora_ids", L + 1),
+                    num_tokens_per_lora=self._view("num_tokens_per_lora", L + 1),
+                    lora_token_start_loc=self._view("lora_token_start_loc", L + 2),
+                    no_lora_flag=self._view("no_lora_flag", 1),
+                    status=self._view("status", 1))
+
+
+def lora_prepare_meta(mapping, meta: LoraMeta, stream=None) -> None:
+    """mapping: int32 device tensor [N] of LoRA ids (-1 = none)."""
+    n = mapping.numel()
+    _check(lib.lora_prepare_meta(mapping.data_ptr() if n else None, n, ctypes.byref(meta.struct),
+                                 _stream(stream)), "lora_prepare_meta")
+
+
+def lora_shrink(x, lora_a: Sequence, buf, meta: LoraMeta, scale: float, stream=None) -> None:
+    """buf[i][t] += scale * x[t] @ lora_a[i][id_t]^T.
+    x bf16 [N][H] (row stride x.stride(0)); lora_a: bf16 [max_loras][r][H] per
+    slice; buf fp32 [S][N][r] contiguous."""
+    n, h = x.shape
+    r = lora_a[0].shape[1]
+    ptrs = _ptr_array(lora_a)
+    _check(lib.lora_shrink(x.data_ptr(), x.stride(0), n, h, ptrs, len(lora_a), r, buf.data_ptr(),
+                           ctypes.byref(meta.struct), float(scale), _stream(stream)), "lora_shrink")
+
+
+def lora_expand(buf, lora_b: Sequence, bias: Optional[Sequence], y, meta: LoraMeta,
+                offset_start: int = 0, add_inputs: bool = True, stream=None) -> None:
+    """y[t, off_i:off_i+O_i] = (add_inputs ? y : 0) + buf[i][t] @ lora_b[i][id_t]^T + bias[i][id_t].
+    buf fp32 [S][N][r]; lora_b bf16 [max_loras][O_i][r] per slice; bias None
+    or per slice (None | bf16 [max_loras][O_i]); y bf16 [N][ldy]."""
+    s, n, r = buf.shape
+    widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
+    bptrs = _ptr_array(lora_b)
+    biasptrs = None if bias is None else _ptr_array(bias)
+    _check(lib.lora_expand(buf.data_ptr(), n, r, bptrs, biasptrs, widths, s, y.data_ptr(), y.stride(0),
+                           int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
+                           _stream(stream)), "lora_expand")

@@ -1,0 +1,212 @@
+// lora_api.hip -- the C ABI of liblora_mi355x.so: argument checks on the host
+// (before any HIP call, so a rejected call launches nothing), metadata region
+// layout, and launch of the gfx950 kernels.  Declarations and the full
+// contract are in include/lora_mi355x.h.
+#include <stdlib.h>
+#include <string.h>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char *name) {
+    const char *e = getenv(name);
+    return e ? atoi(e) : 0;
+}
+
+MetaView view_of(const lora_meta_t *m) {
+    MetaView v;
+    v.sorted = m->token_indices_sorted;
+    v.active_ids = m->active_lora_ids;
+    v.counts = m->num_tokens_per_lora;
+    v.start_loc = m->lora_token_start_loc;
+    v.no_lora = m->no_lora_flag;
+    v.nslots = m->max_loras + 1;
+    return v;
+}
+
+int check_meta(const lora_meta_t *m) {
+    if (!m) return LORA_ERR_NULL;
+    if (!m->token_lora_mapping || !m->token_indices_sorted || !m->active_lora_ids ||
+        !m->num_tokens_per_lora || !m->lora_token_start_loc || !m->no_lora_flag || !m->status)
+        return LORA_ERR_NULL;
+    if (m->max_loras < 1 || m->max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
+    if (m->max_num_tokens < 0) return LORA_ERR_NUM_TOKENS;
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
+    if (max_loras < 1 || max_loras > LORA_MAX_LORAS || max_num_tokens < 0) return 0;
+    const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
+    return 2 * tok + 2 * round_up(sizeof(int32_t) * (max_loras + 1)) +
+           round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign;
+}
+
+int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out) {
+    if (!dev || !out) return LORA_ERR_NULL;
+    if (max_loras < 1 || max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
+    if (max_num_tokens < 0) return LORA_ERR_NUM_TOKENS;
+    if ((reinterpret_cast<uintptr_t>(dev) & (kAlign - 1)) != 0) return LORA_ERR_BUFFER;
+    const size_t need = lora_meta_bytes(max_loras, max_num_tokens);
+    if (bytes < need) return LORA_ERR_BUFFER;
+    char *p = static_cast<char *>(dev);
+    const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
+    const size_t ids = round_up(sizeof(int32_t) * (max_loras + 1));
+    out->token_lora_mapping = reinterpret_cast<int32_t *>(p);
+    p += tok;
+    out->token_indices_sorted = reinterpret_cast<int32_t *>(p);
+    p += tok;
+    out->active_lora_ids = reinterpret_cast<int32_t *>(p);
+    p += ids;
+    out->num_tokens_per_lora = reinterpret_cast<int32_t *>(p);
+    p += ids;
+    out->lora_token_start_loc = reinterpret_cast<int32_t *>(p);
+    p += round_up(sizeof(int32_t) * (max_loras + 2));
+    out->no_lora_flag = reinterpret_cast<int32_t *>(p);
+    p += kAlign;
+    out->status = reinterpret_cast<int32_t *>(p);
+    out->host_no_lora = nullptr;
+    out->max_loras = max_loras;
+    out->max_num_tokens = max_num_tokens;
+    out->num_tokens = -1;
+    return LORA_OK;
+}
+
+int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta, hipStream_t stream) {
+    int st = check_meta(meta);
+    if (st) return st;
+    if (num_tokens < 0 || num_tokens > meta->max_num_tokens) return LORA_ERR_NUM_TOKENS;
+    if (num_tokens > 0 && !mapping) return LORA_ERR_NULL;
+
+    PrepareArgs a;
+    a.mapping = mapping;
+    a.mapping_copy = meta->token_lora_mapping;
+    a.sorted = meta->token_indices_sorted;
+    a.active_ids = meta->active_lora_ids;
+    a.counts = meta->num_tokens_per_lora;
+    a.start_loc = meta->lora_token_start_loc;
+    a.no_lora = meta->no_lora_flag;
+    a.status = meta->status;
+    a.num_tokens = num_tokens;
+    a.max_loras = meta->max_loras;
+    if (launch_prepare(a, stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    if (meta->host_no_lora) {
+        if (hipMemcpyAsync(meta->host_no_lora, meta->no_lora_flag, sizeof(int32_t), hipMemcpyDeviceToHost,
+                           stream) != hipSuccess)
+            return LORA_ERR_LAUNCH;
+    }
+    meta->num_tokens = num_tokens;
+    return LORA_OK;
+}
+
+int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const void *const *lora_a,
+                int num_slices, int rank, float *buf, const lora_meta_t *meta, float scale,
+                hipStream_t stream) {
+    int st = check_meta(meta);
+    if (st) return st;
+    if (meta->num_tokens < 0 || num_tokens != meta->num_tokens) return LORA_ERR_NUM_TOKENS;
+    if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_SLICES;
+    if (!lora_a) return LORA_ERR_NULL;
+    if (hidden < 8 || hidden % 8 || ldx < hidden || ldx % 8) return LORA_ERR_SHAPE;
+    if (rank < 8 || rank > LORA_MAX_RANK || rank % 8) return LORA_ERR_SHAPE;
+    if (num_tokens > 0 && (!x || !buf)) return LORA_ERR_NULL;
+    for (int i = 0; i < num_slices; ++i) {
+        if (!lora_a[i]) return LORA_ERR_NULL;
+        if (!aligned16(lora_a[i])) return LORA_ERR_ALIGN;
+    }
+    if (num_tokens == 0) return LORA_OK;
+    if (!aligned16(x) || !aligned16(buf)) return LORA_ERR_ALIGN;
+
+    ShrinkArgs a;
+    memset(&a, 0, sizeof a);
+    a.meta = view_of(meta);
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    for (int i = 0; i < num_slices; ++i) a.a[i] = static_cast<const uint16_t *>(lora_a[i]);
+    a.buf = buf;
+    a.num_tokens = num_tokens;
+    a.hidden = hidden;
+    a.rank = rank;
+    a.rows = num_slices * rank;
+    a.scale = scale;
+    if (launch_shrink(a, env_int("LORA_SHRINK_TILE_TOKENS"), env_int("LORA_SHRINK_WAVES_K"), stream) != hipSuccess)
+        return LORA_ERR_LAUNCH;
+    return LORA_OK;
+}
+
+int lora_expand(const float *buf, int num_tokens, int rank, const void *const *lora_b, const void *const *bias,
+                const int *slice_widths, int num_slices, void *y, int64_t ldy, int offset_start, int add_inputs,
+                const lora_meta_t *meta, hipStream_t stream) {
+    int st = check_meta(meta);
+    if (st) return st;
+    if (meta->num_tokens < 0 || num_tokens != meta->num_tokens) return LORA_ERR_NUM_TOKENS;
+    if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_SLICES;
+    if (!lora_b || !slice_widths) return LORA_ERR_NULL;
+    if (rank < 8 || rank > LORA_MAX_RANK || rank % 8) return LORA_ERR_SHAPE;
+    if (ldy < 8 || ldy % 8 || offset_start < 0 || offset_start % 8) return LORA_ERR_SHAPE;
+    int64_t total = offset_start;
+    for (int i = 0; i < num_slices; ++i) {
+        if (slice_widths[i] <= 0 || slice_widths[i] % 8) return LORA_ERR_SHAPE;
+        total += slice_widths[i];
+        if (!lora_b[i]) return LORA_ERR_NULL;
+        if (!aligned16(lora_b[i])) return LORA_ERR_ALIGN;
+        if (bias && bias[i] && !aligned16(bias[i])) return LORA_ERR_ALIGN;
+    }
+    if (total > ldy) return LORA_ERR_SHAPE;
+    if (num_tokens > 0 && (!buf || !y)) return LORA_ERR_NULL;
+    if (num_tokens == 0) return LORA_OK;
+    if (!aligned16(buf) || !aligned16(y)) return LORA_ERR_ALIGN;
+
+    ExpandArgs a;
+    memset(&a, 0, sizeof a);
+    a.meta = view_of(meta);
+    a.buf = buf;
+    int off = offset_start;
+    for (int i = 0; i < num_slices; ++i) {
+        a.b[i] = static_cast<const uint16_t *>(lora_b[i]);
+        a.bias[i] = bias ? static_cast<const uint16_t *>(bias[i]) : nullptr;
+        a.width[i] = slice_widths[i];
+        a.col_off[i] = off;
+        off += slice_widths[i];
+    }
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = ldy;
+    a.num_slices = num_slices;
+    a.num_tokens = num_tokens;
+    a.rank = rank;
+    a.add_inputs = add_inputs ? 1 : 0;
+    a.tile_tokens = env_int("LORA_EXPAND_TILE_TOKENS");
+    if (a.tile_tokens % 16) a.tile_tokens = 0;
+    if (launch_expand(a, stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    return LORA_OK;
+}
+
+const char *lora_status_string(int status) {
+    switch (status) {
+        case LORA_OK: return "ok";
+        case LORA_ERR_NULL: return "a required pointer is NULL";
+        case LORA_ERR_NUM_TOKENS: return "num_tokens out of range or different from the prepared batch";
+        case LORA_ERR_SHAPE: return "hidden, rank, slice width or leading dimension out of range";
+        case LORA_ERR_MAX_LORAS: return "max_loras out of range";
+        case LORA_ERR_BUFFER: return "metadata region too small or not 256-byte aligned";
+        case LORA_ERR_ALIGN: return "operand not 16-byte aligned";
+        case LORA_ERR_SLICES: return "num_slices out of range";
+        case LORA_ERR_LAUNCH: return "HIP launch failed";
+        case LORA_ERR_ID_RANGE: return "a LoRA id was outside [-1, max_loras) and was treated as -1";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

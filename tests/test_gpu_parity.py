@@ -1,0 +1,301 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Metadata must match bit for bit; the fp32 shrink buffer and the bf16 expand
+output within the tolerances stated in _harness.py; tokens with id -1 and
+columns outside the slices must be left bit-for-bit untouched.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    from segmented_gather_lora_amd import _build
+    _build.ensure_built()
+    torch.cuda.set_device(0)
+    yield
+
+
+def _prep(mapping: np.ndarray, max_loras: int, max_num_tokens=None):
+    sgl = H.lib()
+    meta = sgl.LoraMeta(max_loras, max_num_tokens or max(mapping.size, 1))
+    sgl.lora_prepare_meta(torch.from_numpy(np.ascontiguousarray(mapping, np.int32)).to("cuda"), meta)
+    torch.cuda.synchronize()
+    return meta
+
+
+# ------------------------------------------------------------------ metadata
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_prepare_workload_mappings(name):
+    spec = workloads.WORKLOADS[name]
+    m = workloads.make_mapping(spec, torch.Generator().manual_seed(spec.seed)).numpy()
+    print("prepare", name, m.size, flush=True)
+    H.check_meta(_prep(m, spec.max_loras), m, spec.max_loras)
+
+
+@pytest.mark.parametrize("seed,n,ml,neg", [
+    (1, 1, 1, 0.0), (2, 63, 3, 0.3), (3, 64, 3, 0.3), (4, 65, 7, 0.3), (5, 1023, 32, 0.1),
+    (6, 1024, 32, 0.0), (7, 1025, 128, 0.2), (8, 5000, 1023, 0.2), (9, 20000, 64, 0.05),
+    (10, 3000, 1, 0.5), (11, 2049, 255, 0.0), (12, 777, 511, 0.9)])
+def test_prepare_random(seed, n, ml, neg):
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, ml, n).astype(np.int32)
+    m[rng.random(n) < neg] = -1
+    print("prepare random", seed, n, ml, flush=True)
+    H.check_meta(_prep(m, ml), m, ml)
+
+
+def test_prepare_skewed_and_sorted_inputs():
+    # one id for everything; already sorted; reverse sorted; alternating
+    for m in [np.zeros(4096, np.int32), np.sort(np.random.default_rng(1).integers(-1, 9, 3000)).astype(np.int32),
+              np.sort(np.random.default_rng(2).integers(-1, 9, 3000))[::-1].astype(np.int32),
+              (np.arange(2500) % 2).astype(np.int32)]:
+        H.check_meta(_prep(m, 9), m, 9)
+
+
+def test_prepare_worked_example_multiset():
+    ids = np.array([-1] * 3 + [0] * 10 + [2] * 5 + [1] * 2, np.int32)
+    m = ids[np.random.default_rng(7).permutation(ids.size)]
+    got = H.check_meta(_prep(m, 3), m, 3)
+    assert got["active_lora_ids"].tolist() == [-1, 0, 1, 2]
+    assert got["num_tokens_per_lora"].tolist() == [3, 10, 2, 5]
+    assert got["lora_token_start_loc"].tolist() == [0, 3, 13, 15, 20]
+
+
+@pytest.mark.parametrize("n", [0, 1, 1000, 16384])
+def test_prepare_no_lora_leaves_buffers(n):
+    sgl = H.lib()
+    meta = sgl.LoraMeta(5, 16384)
+    v = meta.views()
+    for k in ("token_lora_mapping", "token_indices_sorted"):
+        v[k].fill_(12345)
+    for k in ("active_lora_ids", "num_tokens_per_lora", "lora_token_start_loc"):
+        v[k].fill_(7)
+    sgl.lora_prepare_meta(torch.full((n,), -1, dtype=torch.int32, device="cuda"), meta)
+    torch.cuda.synchronize()
+    got = H.meta_numpy(meta, 16384)
+    assert got["no_lora_flag"][0] == 1 and got["status"][0] == 0
+    assert np.all(got["active_lora_ids"] == -1) and np.all(got["num_tokens_per_lora"] == 0)
+    assert np.all(got["lora_token_start_loc"] == 0)
+    assert np.all(got["token_lora_mapping"] == 12345) and np.all(got["token_indices_sorted"] == 12345)
+    assert meta.num_tokens == n
+
+
+def test_prepare_bad_ids_reported():
+    m = np.array([0, 5, -2, 1, 1, 2, 77, -1], np.int32)
+    H.check_meta(_prep(m, 3), m, 3)
+
+
+def test_prepare_reuse_and_determinism():
+    sgl = H.lib()
+    meta = sgl.LoraMeta(64, 8192)
+    big = np.random.default_rng(3).integers(-1, 64, 8192).astype(np.int32)
+    small = np.array([3, 3, -1, 0], np.int32)
+    for m in (big, small, big):
+        sgl.lora_prepare_meta(torch.from_numpy(m).cuda(), meta)
+        torch.cuda.synchronize()
+        H.check_meta(meta, m, 64)
+    a = H.meta_numpy(meta, 8192)
+    sgl.lora_prepare_meta(torch.from_numpy(big).cuda(), meta)
+    torch.cuda.synchronize()
+    b = H.meta_numpy(meta, 8192)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+
+
+def test_host_mirror_of_flag():
+    sgl = H.lib()
+    meta = sgl.LoraMeta(4, 64)
+    host = torch.full((1,), 99, dtype=torch.int32, pin_memory=True)
+    meta.struct.host_no_lora = host.data_ptr()
+    sgl.lora_prepare_meta(torch.full((10,), -1, dtype=torch.int32, device="cuda"), meta)
+    torch.cuda.synchronize()
+    assert int(host[0]) == 1
+    sgl.lora_prepare_meta(torch.tensor([0, -1, 2], dtype=torch.int32, device="cuda"), meta)
+    torch.cuda.synchronize()
+    assert int(host[0]) == 0
+    meta.struct.host_no_lora = None
+
+
+# ------------------------------------------------------------------ shrink + expand
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+@pytest.mark.parametrize("name,n", [("tiny", None), ("decode", 200), ("prefill", 600), ("zipf", 300),
+                                    ("large", 160)])
+def test_parity_all_tokens(name, n, add_inputs):
+    wl = workloads.make_workload(name, num_tokens=n)
+    print("parity", name, n, add_inputs, flush=True)
+    st = H.run_and_check(wl, add_inputs=add_inputs)
+    print(st, flush=True)
+
+
+@pytest.mark.parametrize("name,sample", [("decode", None), ("prefill", 96), ("zipf", 96), ("large", 64)])
+def test_parity_full_size_sampled(name, sample):
+    wl = workloads.make_workload(name)
+    print("full size", name, flush=True)
+    st = H.run_and_check(wl, add_inputs=True, sample=sample, seed=11)
+    print(st, flush=True)
+
+
+def test_no_lora_full_size_touches_nothing():
+    wl = workloads.make_workload("large_nolora")
+    print("no-lora full size", flush=True)
+    H.run_and_check(wl, add_inputs=True, sample=32)
+
+
+@pytest.mark.parametrize("name,n", [("tiny", None), ("decode", None), ("prefill", 700), ("zipf", 400),
+                                    ("large", 300)])
+@pytest.mark.parametrize("add_inputs", [True, False])
+def test_expand_only_synthetic_buffer(name, n, add_inputs):
+    wl = workloads.make_workload(name, num_tokens=n)
+    print("expand only", name, n, add_inputs, flush=True)
+    print(H.run_expand_only(wl, add_inputs), flush=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=101, n=1, hidden=64, slices=(8,), rank=8, max_loras=1, neg_fraction=0.0),
+    dict(seed=102, n=37, hidden=72, slices=(24, 40), rank=24, max_loras=5, bias=True),
+    dict(seed=103, n=130, hidden=200, slices=(264, 8, 520), rank=40, max_loras=9, bias=True),
+    dict(seed=104, n=257, hidden=8, slices=(16,), rank=128, max_loras=3),
+    dict(seed=105, n=90, hidden=136, slices=(8,) * 8, rank=16, max_loras=17, bias=True),
+    dict(seed=106, n=500, hidden=1032, slices=(1032, 72), rank=56, max_loras=200),
+    dict(seed=107, n=64, hidden=96, slices=(96,), rank=104, max_loras=2, neg_fraction=0.0),
+])
+def test_edge_shapes(case):
+    wl = workloads.random_case(**case)
+    print("edge", case, flush=True)
+    H.run_and_check(wl, add_inputs=True)
+    H.run_and_check(wl, add_inputs=False)
+
+
+def test_offset_start_and_wide_rows():
+    wl = workloads.random_case(111, 70, 64, (32, 16, 40), 16, 6, bias=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=24, ldy_extra=40)
+    H.run_and_check(wl, add_inputs=False, offset_start=8, ldy_extra=8)
+
+
+@pytest.mark.parametrize("tile,wk,ks", [(16, 1, 1), (16, 2, 3), (16, 4, 1), (32, 1, 2), (32, 2, 1),
+                                        (32, 4, 4), (64, 1, 1), (64, 2, 2), (64, 4, 3)])
+def test_shrink_tile_variants(tile, wk, ks, monkeypatch):
+    monkeypatch.setenv("LORA_SHRINK_TILE_TOKENS", str(tile))
+    monkeypatch.setenv("LORA_SHRINK_WAVES_K", str(wk))
+    monkeypatch.setenv("LORA_SHRINK_KSPLIT", str(ks))
+    wl = workloads.random_case(120 + tile + wk, 333, 520, (96, 40, 8), 24, 11, bias=True)
+    print("shrink variant", tile, wk, ks, flush=True)
+    H.run_and_check(wl, add_inputs=True)
+
+
+@pytest.mark.parametrize("tt", [16, 48, 128, 256])
+def test_expand_tile_variants(tt, monkeypatch):
+    monkeypatch.setenv("LORA_EXPAND_TILE_TOKENS", str(tt))
+    wl = workloads.random_case(130 + tt, 700, 64, (520, 264), 32, 5, bias=True, neg_fraction=0.1)
+    print("expand variant", tt, flush=True)
+    H.run_and_check(wl, add_inputs=True)
+
+
+def _gpu_outputs(wl, meta, buf0=None):
+    sgl = H.lib()
+    L = wl.layers[0]
+    D = H.DevLayer(L)
+    n = wl.mapping.numel()
+    buf = torch.zeros((len(L.spec.slices), n, L.spec.rank), dtype=torch.float32, device="cuda")
+    if buf0 is not None:
+        buf.copy_(buf0)
+    sgl.lora_shrink(D.x, D.a, buf, meta, L.spec.scale)
+    y = D.y0.clone()
+    sgl.lora_expand(buf, D.b, D.bias, y, meta, add_inputs=True)
+    torch.cuda.synchronize()
+    return buf.cpu().numpy(), H.bits(y)
+
+
+def test_segment_order_invariance(monkeypatch):
+    """Kernels must not assume ascending segments: metadata written by hand in
+    the order of the pages' worked example ([-1, 0, 2, 1]) gives the same result."""
+    monkeypatch.setenv("LORA_SHRINK_KSPLIT", "1")
+    ids = np.array([-1] * 3 + [0] * 10 + [2] * 5 + [1] * 2, np.int32)
+    m = ids[np.random.default_rng(9).permutation(ids.size)]
+    wl = workloads.random_case(140, 20, 128, (64, 32), 16, 3, bias=True)
+    wl.mapping.copy_(torch.from_numpy(m))
+    meta = _prep(m, 3)
+    buf_a, y_a = _gpu_outputs(wl, meta)
+    v = meta.views()
+    order = [-1, 0, 2, 1]
+    srt = np.concatenate([np.nonzero(m == k)[0] for k in order]).astype(np.int32)
+    cnt = [int((m == k).sum()) for k in order]
+    v["active_lora_ids"].copy_(torch.tensor(order, dtype=torch.int32))
+    v["num_tokens_per_lora"].copy_(torch.tensor(cnt, dtype=torch.int32))
+    v["lora_token_start_loc"].copy_(torch.tensor([0] + list(np.cumsum(cnt)), dtype=torch.int32))
+    assert v["lora_token_start_loc"].tolist() == [0, 3, 13, 18, 20]
+    v["token_indices_sorted"][:20].copy_(torch.from_numpy(srt))
+    buf_b, y_b = _gpu_outputs(wl, meta)
+    assert np.array_equal(buf_a, buf_b) and np.array_equal(y_a, y_b)
+
+
+def test_permutation_equivariance(monkeypatch):
+    monkeypatch.setenv("LORA_SHRINK_KSPLIT", "1")
+    wl = workloads.random_case(150, 300, 256, (128, 64), 32, 7, bias=True)
+    m = wl.mapping.numpy()
+    buf_a, y_a = _gpu_outputs(wl, _prep(m, 7))
+    perm = np.random.default_rng(4).permutation(300)
+    L = wl.layers[0]
+    wl2 = workloads.Workload(wl.spec, wl.mapping[perm].clone(), [workloads.Layer(
+        L.spec, L.x[perm].clone(), L.lora_a, L.lora_b, L.bias, L.y0[perm].clone())])
+    buf_b, y_b = _gpu_outputs(wl2, _prep(m[perm], 7))
+    assert np.array_equal(buf_b, buf_a[:, perm]) and np.array_equal(y_b, y_a[perm])
+
+
+def test_shrink_accumulates_into_buffer():
+    wl = workloads.random_case(160, 90, 192, (32, 16), 16, 4)
+    L = wl.layers[0]
+    m = wl.mapping.numpy()
+    meta = _prep(m, 4)
+    gen = torch.Generator().manual_seed(5)
+    buf0 = torch.randn((2, 90, 16), generator=gen)
+    sgl = H.lib()
+    buf = buf0.cuda()
+    sgl.lora_shrink(L.x.cuda(), [a.cuda() for a in L.lora_a], buf, meta, L.spec.scale)
+    torch.cuda.synchronize()
+    ref = buf0.numpy().copy()
+    st, bound = oracle.shrink(workloads.bf16_bits(L.x), [workloads.bf16_bits(a) for a in L.lora_a], ref, m,
+                              L.spec.scale, 4, with_bound=True)
+    H.shrink_check(buf.cpu().numpy(), ref, bound)
+    neg = m == -1
+    assert np.array_equal(buf.cpu().numpy()[:, neg], buf0.numpy()[:, neg])
+
+
+def test_bad_ids_are_not_touched():
+    m = np.array([0, 9, 1, -5, 2, 2, 0, 100] * 4, np.int32)
+    wl = workloads.random_case(170, m.size, 64, (16,), 8, 3)
+    wl.mapping.copy_(torch.from_numpy(m))
+    meta = _prep(m, 3)
+    assert int(meta.views()["status"][0]) == H.lib().LORA_ERR_ID_RANGE
+    buf, y = _gpu_outputs(wl, meta)
+    bad = (m < -1) | (m >= 3)
+    assert np.all(buf[:, bad] == 0)
+    assert np.array_equal(y[bad], workloads.bf16_bits(wl.layers[0].y0)[bad])
+
+
+def test_invalid_arguments_raise():
+    sgl = H.lib()
+    meta = _prep(np.zeros(8, np.int32), 2)
+    x = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    a = [torch.zeros((2, 16, 64), dtype=torch.bfloat16, device="cuda")]
+    buf = torch.zeros((1, 8, 16), device="cuda")
+    with pytest.raises(sgl.LoraError) as e:
+        sgl.lora_shrink(x[:7], a, buf, meta, 1.0)
+    assert e.value.status == sgl.LORA_ERR_NUM_TOKENS
+    with pytest.raises(sgl.LoraError) as e:
+        sgl.lora_shrink(x, [torch.zeros((2, 12, 64), dtype=torch.bfloat16, device="cuda")], buf, meta, 1.0)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    with pytest.raises(sgl.LoraError):
+        sgl.lora_prepare_meta(torch.zeros(9, dtype=torch.int32, device="cuda"), meta)

@@ -116,9 +116,10 @@ def make_mapping(spec: WorkloadSpec, gen: torch.Generator) -> torch.Tensor:
     elif kind == "uniform":
         m = torch.randint(0, ml, (n,), generator=gen, dtype=torch.int64)
     elif kind == "runs":
-        runs, run_len = 16, n // 16
+        runs = 16
         ids = torch.randint(0, ml, (runs,), generator=gen, dtype=torch.int64)
-        m = ids.repeat_interleave(run_len)
+        lens = torch.tensor([n // runs + (1 if i < n % runs else 0) for i in range(runs)])
+        m = ids.repeat_interleave(lens)
     elif kind == "zipf":
         p = torch.arange(1, ml + 1, dtype=torch.float64).pow(-1.1)
         m = torch.multinomial(p / p.sum(), n, replacement=True, generator=gen)
