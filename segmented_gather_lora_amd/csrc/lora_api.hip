@@ -141,8 +141,13 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     a.rank = rank;
     a.rows = num_slices * rank;
     a.scale = scale;
-    if (launch_shrink(a, env_int("LORA_SHRINK_TILE_TOKENS"), env_int("LORA_SHRINK_WAVES_K"), stream) != hipSuccess)
-        return LORA_ERR_LAUNCH;
+    ShrinkTuning cfg;
+    cfg.tile_tokens = env_int("LORA_SHRINK_TILE_TOKENS");
+    cfg.waves_k = env_int("LORA_SHRINK_WAVES_K");
+    cfg.mtiles_per_wave = env_int("LORA_SHRINK_MTILES");
+    cfg.k_splits = env_int("LORA_SHRINK_KSPLIT");
+    cfg.grid_cap = env_int("LORA_SHRINK_GRID");
+    if (launch_shrink(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }
 
@@ -187,9 +192,11 @@ int lora_expand(const float *buf, int num_tokens, int rank, const void *const *l
     a.num_tokens = num_tokens;
     a.rank = rank;
     a.add_inputs = add_inputs ? 1 : 0;
-    a.tile_tokens = env_int("LORA_EXPAND_TILE_TOKENS");
-    if (a.tile_tokens % 16) a.tile_tokens = 0;
-    if (launch_expand(a, stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    ExpandTuning cfg;
+    cfg.tile_tokens = env_int("LORA_EXPAND_TILE_TOKENS");
+    if (cfg.tile_tokens % 16) cfg.tile_tokens = 0;
+    cfg.grid_cap = env_int("LORA_EXPAND_GRID");
+    if (launch_expand(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }
 

@@ -19,6 +19,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Wave index within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -80,41 +83,101 @@ struct MetaView {
     int32_t nslots;              // max_loras + 1
 };
 
-// Map a linear tile index `u` onto (slot, tile-within-slot) where every slot
-// with an id other than -1 owns ceil(count / tile_tokens) tiles, in slot
-// order.  Computed by each wave on its own from the metadata (no barrier).
-// Returns false when `u` is past the last tile.
-__device__ __forceinline__ bool find_tile(const MetaView &m, int tile_tokens, int u,
-                                          int &slot, int &tile, int &seg_start, int &seg_count, int &lora_id) {
-    int base = 0;
-    const int lane = lane_id();
-    for (int c0 = 0; c0 < m.nslots; c0 += kWave) {
-        int k = c0 + lane;
-        int n_tiles = 0;
-        int cnt = 0, id = -1;
-        if (k < m.nslots) {
-            cnt = m.counts[k];
-            id = m.active_ids[k];
-            if (id >= 0) n_tiles = (cnt + tile_tokens - 1) / tile_tokens;
+constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Per-workgroup table of work tiles, built in LDS from the metadata: every
+// slot whose id is not -1 owns ceil(count / tile_tokens) tiles, in slot order
+// (so no order of the segments is assumed).  Layout in `smem` (ints):
+//   pre[nslots + 1]  exclusive prefix of tiles per slot (pre[nslots] = total)
+//   sid[nslots], sstart[nslots], scnt[nslots]
+// All threads of the block must call it; returns the total number of tiles.
+__device__ __forceinline__ int tile_table_ints(int nslots) { return 4 * nslots + 1; }
+
+__device__ __forceinline__ int build_tile_table(const MetaView &m, int tile_tokens, int *smem, int *s_wsum) {
+    const int nslots = m.nslots;
+    int *pre = smem, *sid = smem + nslots + 1, *sst = sid + nslots, *scn = sst + nslots;
+    const int nthreads = blockDim.x, tid = threadIdx.x;
+    const int per = (nslots + nthreads - 1) / nthreads;
+    const int beg = tid * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+        const int k = beg + i;
+        if (k < nslots) {
+            const int id = m.active_ids[k], c = m.counts[k];
+            const int nt = id >= 0 ? (c + tile_tokens - 1) / tile_tokens : 0;
+            sid[k] = id;
+            scn[k] = c;
+            sst[k] = nt ? m.start_loc[k] : 0;
+            pre[k] = nt;   // temporarily the tile count
+            sum += nt;
         }
-        int incl = wave_inclusive_scan(n_tiles);
-        int excl = incl - n_tiles;
-        bool hit = (n_tiles > 0) && (u >= base + excl) && (u < base + incl);
-        uint64_t hm = ballot(hit);
-        if (hm) {
-            int src = __ffsll((long long)hm) - 1;
-            slot = c0 + src;
-            int e = __shfl(excl, src, kWave);
-            tile = u - base - e;
-            seg_count = __shfl(cnt, src, kWave);
-            lora_id = __shfl(id, src, kWave);
-            seg_start = m.start_loc[slot];
-            return true;
-        }
-        base += __shfl(incl, kWave - 1, kWave);
     }
-    return false;
+    const int lane = lane_id(), wave = tid / kWave, nwaves = nthreads / kWave;
+    const int incl = wave_inclusive_scan(sum);
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        const int v = s_wsum[w];
+        base += w < wave ? v : 0;
+        total += v;
+    }
+    int run = base + incl - sum;
+    for (int i = 0; i < per; ++i) {
+        const int k = beg + i;
+        if (k < nslots) {
+            const int nt = pre[k];
+            pre[k] = run;
+            run += nt;
+        }
+    }
+    if (tid == 0) pre[nslots] = total;
+    __syncthreads();
+    return total;
 }
+
+struct TileRef {
+    int lora_id, seg_start, seg_count, tile;
+};
+
+// Slot of tile `t` (< total): the last k with pre[k] <= t (binary search; the
+// argument is uniform across the wave, so every read is an LDS broadcast).
+__device__ __forceinline__ TileRef lookup_tile(const int *smem, int nslots, int t) {
+    const int *pre = smem, *sid = smem + nslots + 1, *sst = sid + nslots, *scn = sst + nslots;
+    int lo = 0, hi = nslots - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    TileRef r;
+    r.lora_id = sid[lo];
+    r.seg_start = sst[lo];
+    r.seg_count = scn[lo];
+    r.tile = t - pre[lo];
+    return r;
+}
+
+// Units are numbered in a canonical order (tile-major) and cut into kNumXcd
+// contiguous chunks; workgroup b (on XCD b % 8) walks chunk b % 8, so
+// neighbouring units -- the tiles of one segment, or the row/column blocks of
+// one tile -- run on the same XCD and share its L2.
+struct UnitWalker {
+    int chunk, first, stride, limit, xcd;
+    __device__ __forceinline__ UnitWalker(int units) {
+        chunk = (units + kNumXcd - 1) / kNumXcd;
+        xcd = blockIdx.x % kNumXcd;
+        first = blockIdx.x / kNumXcd;
+        stride = gridDim.x / kNumXcd;
+        limit = units;
+    }
+    // unit index for the i-th step of this workgroup, or -1 when done
+    __device__ __forceinline__ int unit(int j) const {
+        if (j >= chunk) return -1;
+        const int u = xcd * chunk + j;
+        return u < limit ? u : -1;
+    }
+};
 
 // ---------------------------------------------------------------- kernel args
 
@@ -167,9 +230,23 @@ struct ExpandArgs {
     int32_t add_inputs;
 };
 
+// Launch-geometry overrides (0 = automatic), read from the environment by the
+// API layer for tuning sweeps; they change tiling only, never the result.
+struct ShrinkTuning {
+    int tile_tokens;       // 16, 32, 64 or 128
+    int waves_k;           // 1, 2 or 4
+    int mtiles_per_wave;   // 1..4
+    int k_splits;
+    int grid_cap;
+};
+struct ExpandTuning {
+    int tile_tokens;       // 16, 32 or 64
+    int grid_cap;
+};
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
-hipError_t launch_shrink(const ShrinkArgs &a, int tokens_per_tile, int waves_k, hipStream_t s);
-hipError_t launch_expand(const ExpandArgs &a, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream_t s);
+hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream_t s);
 
 }  // namespace lora
