@@ -30,6 +30,7 @@ MetaView view_of(const lora_meta_t *m) {
     v.start_loc = m->lora_token_start_loc;
     v.no_lora = m->no_lora_flag;
     v.nslots = m->max_loras + 1;
+    v.lds_tokens = 0;
     return v;
 }
 
@@ -147,6 +148,8 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     cfg.mtiles_per_wave = env_int("LORA_SHRINK_MTILES");
     cfg.k_splits = env_int("LORA_SHRINK_KSPLIT");
     cfg.grid_cap = env_int("LORA_SHRINK_GRID");
+    cfg.variant = env_int("LORA_SHRINK_VARIANT");
+    cfg.staged_cfg = env_int("LORA_SHRINK_STAGED");
     if (launch_shrink(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }

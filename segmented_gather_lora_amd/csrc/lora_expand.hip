@@ -4,28 +4,28 @@
 // PunicaWrapperTPU.add_expand and the bias rule of PunicaWrapperTPU._apply_bias
 // on the "punica_tpu" page, folded into one pass with a single rounding).
 //
-// Per segment and slice this is C[cols][tokens] = B_id[cols][r] * buf_seg[tokens][r]^T
-// with K = r (8..128), on the bf16 MFMA (v_mfma_f32_16x16x32_bf16):
-//   - each wave owns 64 output columns of one slice; a workgroup (4 waves)
-//     covers 256 columns, and a work unit is (TT tiles of 16 tokens of one
-//     segment) x (256 columns);
-//   - the wave loads its weights (64 x r) once per unit, then, for all TT
-//     token tiles at once, the token indices and afterwards the fp32 buffer
-//     rows and the y rows, so a unit costs two memory round trips;
-//   - each fp32 buffer value is split into bf16 hi = rne(v) and lo = rne(v - hi)
-//     and both parts go through the MFMA, keeping ~16 mantissa bits;
-//   - the 64 columns are permuted onto the four 16-row MFMA tiles so that a
-//     lane ends with 16 consecutive columns of one token: y is read and
-//     written as 32 contiguous bytes per lane (128 per token row per wave).
+// Per segment and slice this is C[tokens][cols] = buf_seg[tokens][r] * B_id[cols][r]^T
+// with K = r (8..128), on the bf16 MFMA (v_mfma_f32_16x16x32_bf16) with the
+// tokens on the M side and the output columns on the N side:
+//   - a work unit is (TT tiles of 16 tokens of one segment) x (256 columns of
+//     one slice); each of the 4 waves owns 64 of the columns and keeps their
+//     weights (64 x r bf16) in registers for the unit;
+//   - the unit's fp32 buffer rows are read once per workgroup with coalesced
+//     loads, split into bf16 hi = rne(v) and lo = rne(v - hi) and staged in
+//     LDS; every wave reads its MFMA operands from there, and both parts go
+//     through the MFMA, which keeps ~16 mantissa bits of the fp32 value;
+//   - the 64 columns of a wave are spread over four 16-column MFMA tiles so
+//     that lane n holds columns 4n..4n+3 of 4 tokens: every y load and store
+//     instruction moves 128 contiguous bytes of 4 token rows.
 // Work units follow a canonical tile-major order cut into one chunk per XCD,
 // walked by a persistent grid.
 //
-// Loads are unconditional.  A lane whose token is past the end of the
-// segment works on the segment's last token, and an 8-column group past the
-// end of the slice works on the slice's last 8 columns: such a lane computes
-// exactly the values of the lane that owns that data and stores them to the
-// same address, so the duplicate store is harmless.  Tokens with id -1 own no
-// tile and are never touched.
+// No load or store is conditional.  A lane whose token is past the end of
+// the segment works on the segment's last token, and a 4-column group past
+// the end of the slice works on the slice's last 4 columns: it computes
+// exactly the owner's values and stores them to the same address, so the
+// duplicate store is harmless.  Tokens with id -1 own no tile and are never
+// touched.
 #include "lora_internal.h"
 
 namespace lora {
@@ -33,8 +33,9 @@ namespace lora {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kWaveCols = 64;
-constexpr int kBlockCols = 4 * kWaveCols;
+constexpr int kBlockCols = kWaves * kWaveCols;
 
 template <typename T, int N>
 __device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
@@ -45,39 +46,31 @@ __device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
     return r;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 
-// Split 8 floats into bf16 hi and lo operands.
-__device__ __forceinline__ void split_bf16(const floatx4 &v0, const floatx4 &v1, u32x4 &hi, u32x4 &lo) {
-    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = float_to_bf16_bits(v[e]);
-        l[e] = float_to_bf16_bits(v[e] - bf16_bits_to_float(h[e]));
-    }
-    hi = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-    lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
-}
-
-// Column a lane works on for slice column c: itself when inside the slice,
-// else the same position in the slice's last 8-column group.
-__device__ __forceinline__ int clamp_col(int c, int width) { return c < width ? c : width - 8 + (c & 7); }
+// Last valid 4-column group for a group starting at c (c % 4 == 0).
+__device__ __forceinline__ int clamp_group(int c, int width) { return c < width ? c : width - 4; }
 
 template <int KS, int TT, bool ADD>
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
+    constexpr int kUnitTokens = 16 * TT;
+    constexpr int kRowK = 32 * KS;              // bf16 per staged row (rank padded to 32)
+    constexpr int kRowStride = kRowK + 8;       // +16 bytes: rows start on different banks
     extern __shared__ int smem[];
-    __shared__ int s_wsum[kThreads / kWave];
+    __shared__ int s_wsum[kWaves];
+    __shared__ __attribute__((aligned(16))) uint16_t s_hi[kUnitTokens * kRowStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_lo[kUnitTokens * kRowStride];
 
     if (*a.meta.no_lora) return;
     const int nslots = a.meta.nslots;
-    constexpr int kUnitTokens = 16 * TT;
     const int total = build_tile_table(a.meta, kUnitTokens, smem, s_wsum);
 
-    const int lane = lane_id(), wave = wave_id();
-    const int col = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int n16 = lane & 15, g = lane >> 4;
+    const int rank = a.rank;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
 
     const UnitWalker walk(total * a.col_blocks);
     for (int jj = walk.first;; jj += walk.stride) {
@@ -85,134 +78,141 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
         if (u < 0) break;
         const int cb = u % a.col_blocks;
         const TileRef tr = lookup_tile(smem, nslots, u / a.col_blocks);
-
         int i = 0;
 #pragma unroll
         for (int s = 1; s < LORA_MAX_SLICES; ++s)
             if (s < a.num_slices && cb >= a.block_begin[s]) i = s;
         const int width = select_slice(a.width, i);
         const int c0 = (cb - select_slice(a.block_begin, i)) * kBlockCols + wave * kWaveCols;
-        if (c0 >= width) continue;   // this wave has no columns in the block (no barrier below)
+        const bool has_cols = c0 < width;   // wave-uniform; every wave still joins the barriers
+        const int cw = has_cols ? c0 : 0;
+        const int pbase = tr.tile * kUnitTokens;
+        const float *bufs = a.buf + (int64_t)i * a.num_tokens * rank;
 
-        // token indices of the unit's TT tiles (past the end: the last token)
-        int tok[TT];
+        // ---- coalesced fp32 buffer loads for the unit's rows: rank/4 lanes per row
+        const int lanes_per_row = rank >> 2;                 // 16-byte pieces per row
+        const int rows_per_pass = kThreads / lanes_per_row;
+        // rank <= 32*KS, so a pass covers at least kThreads / (8*KS) rows
+        constexpr int kMinRowsPerPass = kThreads / (8 * KS);
+        constexpr int kPasses = (kUnitTokens + kMinRowsPerPass - 1) / kMinRowsPerPass;
+        floatx4 bvals[kPasses];
+        int brow_p[kPasses];
 #pragma unroll
-        for (int q = 0; q < TT; ++q) {
-            int p = tr.tile * kUnitTokens + q * 16 + col;
-            p = p < tr.seg_count ? p : tr.seg_count - 1;
-            tok[q] = a.meta.sorted[tr.seg_start + p];
+        for (int ps = 0; ps < kPasses; ++ps) {
+            int p = ps * rows_per_pass + tid / lanes_per_row;
+            const int piece = tid % lanes_per_row;
+            brow_p[ps] = p;
+            p = p < kUnitTokens ? p : kUnitTokens - 1;
+            int pp = pbase + p;
+            pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
+            int t = sorted_at(a.meta, smem, tr.seg_start + pp);
+            t = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
+            bvals[ps] = *reinterpret_cast<const floatx4 *>(bufs + (int64_t)t * rank + 4 * piece);
         }
 
-        // weights: MFMA row `col` of tile mt is output column 16*(col/4) + 4*mt + col%4
-        const uint16_t *wbase = select_slice(a.b, i) + (int64_t)tr.lora_id * width * a.rank;
+        // ---- this wave's weights: B operand of n-tile q, lane (n16, g) -> column 4*n16 + q
+        const int grp = clamp_group(cw + 4 * n16, width);    // first of this lane's 4 columns
+        const uint16_t *wbase = select_slice(a.b, i) + (int64_t)tr.lora_id * width * rank;
         u32x4 w[4][KS];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int c = clamp_col(c0 + 16 * (col >> 2) + 4 * mt + (col & 3), width);
-            const uint16_t *row = wbase + (int64_t)c * a.rank;
+        for (int q = 0; q < 4; ++q) {
+            const uint16_t *row = wbase + (int64_t)(grp + q) * rank;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int k = ks * 32 + 8 * g;
-                w[mt][ks] = *reinterpret_cast<const u32x4 *>(row + (k < a.rank ? k : 0));
+                w[q][ks] = *reinterpret_cast<const u32x4 *>(row + (k < rank ? k : 0));
             }
         }
-        // this lane's output columns: two groups of 8 starting at cl and cl + 8
-        const int cl = c0 + 16 * g;
-        const int cg0 = clamp_col(cl, width), cg1 = clamp_col(cl + 8, width);
         const uint16_t *bptr = select_slice(a.bias, i);
-        u32x4 bias0 = z4, bias1 = z4;
-        if (bptr) {
-            const uint16_t *brow = bptr + (int64_t)tr.lora_id * width;
-            bias0 = *reinterpret_cast<const u32x4 *>(brow + cg0);
-            bias1 = *reinterpret_cast<const u32x4 *>(brow + cg1);
-        }
+        u32x2 braw = {0u, 0u};
+        if (bptr) braw = *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp);
 
-        // guard against metadata that is not from this batch
-        bool tv[TT];
+        // ---- y rows: tile q, row 4g + e of the tile -> token index
+        const int ycol = select_slice(a.col_off, i) + grp;
+        int ytok[TT][4];
+        u32x2 yv[TT][4];
 #pragma unroll
-        for (int q = 0; q < TT; ++q) {
-            tv[q] = (unsigned)tok[q] < (unsigned)a.num_tokens;
-            tok[q] = tv[q] ? tok[q] : 0;
-        }
+        for (int q = 0; q < TT; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int pp = pbase + q * 16 + 4 * g + e;
+                pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
+                int t = sorted_at(a.meta, smem, tr.seg_start + pp);
+                t = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
+                ytok[q][e] = t;
+                if (ADD) yv[q][e] = *reinterpret_cast<const u32x2 *>(a.y + (int64_t)t * a.ldy + ycol);
+                else yv[q][e] = u32x2{0u, 0u};
+            }
 
-        // buffer rows and y rows of all tiles
-        const float *bufs = a.buf + (int64_t)i * a.num_tokens * a.rank;
-        const int ycol = select_slice(a.col_off, i);
-        floatx4 bv[TT][KS][2];
-        u32x4 yv[TT][2];
+        // ---- stage the buffer rows in LDS as bf16 hi / lo (rank tail stays zero)
 #pragma unroll
-        for (int q = 0; q < TT; ++q) {
-            const float *brow = bufs + (int64_t)tok[q] * a.rank;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int k = ks * 32 + 8 * g;
-                const int kc = k < a.rank ? k : 0;
-                bv[q][ks][0] = *reinterpret_cast<const floatx4 *>(brow + kc);
-                bv[q][ks][1] = *reinterpret_cast<const floatx4 *>(brow + kc + 4);
-            }
-            if (ADD) {
-                const uint16_t *yrow = a.y + (int64_t)tok[q] * a.ldy + ycol;
-                yv[q][0] = *reinterpret_cast<const u32x4 *>(yrow + cg0);
-                yv[q][1] = *reinterpret_cast<const u32x4 *>(yrow + cg1);
-            } else {
-                yv[q][0] = z4;
-                yv[q][1] = z4;
-            }
-        }
-
-        // rank tail: K positions >= r contribute nothing
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool kin = ks * 32 + 8 * g < a.rank;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) w[mt][ks] = kin ? w[mt][ks] : z4;
-#pragma unroll
-            for (int q = 0; q < TT; ++q) {
-                bv[q][ks][0] = kin ? bv[q][ks][0] : zf;
-                bv[q][ks][1] = kin ? bv[q][ks][1] : zf;
-            }
-        }
-        float bias[16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bias[2 * e] = bf16_bits_to_float(bias0[e] & 0xffffu);
-            bias[2 * e + 1] = bf16_bits_to_float(bias0[e] >> 16);
-            bias[8 + 2 * e] = bf16_bits_to_float(bias1[e] & 0xffffu);
-            bias[8 + 2 * e + 1] = bf16_bits_to_float(bias1[e] >> 16);
-        }
-
-#pragma unroll
-        for (int q = 0; q < TT; ++q) {
-            floatx4 acc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc[mt] = zf;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 hi, lo;
-                split_bf16(bv[q][ks][0], bv[q][ks][1], hi, lo);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[mt] = mfma16x16x32(as_bf16x8(w[mt][ks]), as_bf16x8(hi), acc[mt]);
-                    acc[mt] = mfma16x16x32(as_bf16x8(w[mt][ks]), as_bf16x8(lo), acc[mt]);
-                }
-            }
-            // acc[mt][e] is column cl + 4*mt + e of token tok[q] (or its duplicate)
-            uint16_t *yrow = a.y + (int64_t)tok[q] * a.ldy + ycol;
-#pragma unroll
-            for (int hgrp = 0; hgrp < 2; ++hgrp) {
-                uint32_t o[4];
+        for (int ps = 0; ps < kPasses; ++ps) {
+            const int p = brow_p[ps];
+            const int piece = tid % lanes_per_row;
+            if (p < kUnitTokens) {
+                uint32_t h[4], l[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c_lo = 8 * hgrp + 2 * e, c_hi = c_lo + 1;
-                    const float d_lo = acc[c_lo >> 2][c_lo & 3] + bias[c_lo];
-                    const float d_hi = acc[c_hi >> 2][c_hi & 3] + bias[c_hi];
-                    const float r_lo = bf16_bits_to_float(yv[q][hgrp][e] & 0xffffu) + d_lo;
-                    const float r_hi = bf16_bits_to_float(yv[q][hgrp][e] >> 16) + d_hi;
-                    o[e] = pack2(float_to_bf16_bits(r_lo), float_to_bf16_bits(r_hi));
+                    h[e] = float_to_bf16_bits(bvals[ps][e]);
+                    l[e] = float_to_bf16_bits(bvals[ps][e] - bf16_bits_to_float(h[e]));
                 }
-                if (tv[q]) *reinterpret_cast<u32x4 *>(yrow + (hgrp ? cg1 : cg0)) = u32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<u32x2 *>(&s_hi[p * kRowStride + 4 * piece]) = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+                *reinterpret_cast<u32x2 *>(&s_lo[p * kRowStride + 4 * piece]) = u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])};
             }
         }
+        if (rank < kRowK) {   // zero the rank padding once per unit
+            for (int x = tid; x < kUnitTokens * (kRowK - rank); x += kThreads) {
+                const int p = x / (kRowK - rank), k = rank + x % (kRowK - rank);
+                s_hi[p * kRowStride + k] = 0;
+                s_lo[p * kRowStride + k] = 0;
+            }
+        }
+        // K positions >= rank: zero the weights too (no NaN from stale data)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool kin = ks * 32 + 8 * g < rank;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q][ks] = kin ? w[q][ks] : z4;
+        }
+        float bias[4];
+        bias[0] = bf16_bits_to_float(braw[0] & 0xffffu);
+        bias[1] = bf16_bits_to_float(braw[0] >> 16);
+        bias[2] = bf16_bits_to_float(braw[1] & 0xffffu);
+        bias[3] = bf16_bits_to_float(braw[1] >> 16);
+        __syncthreads();
+
+        if (has_cols) {
+#pragma unroll
+            for (int q = 0; q < TT; ++q) {
+                floatx4 acc[4];
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) acc[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int off = (q * 16 + n16) * kRowStride + ks * 32 + 8 * g;
+                    const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_hi[off]);
+                    const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lo[off]);
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        acc[t4] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(w[t4][ks]), acc[t4]);
+                        acc[t4] = mfma16x16x32(as_bf16x8(al), as_bf16x8(w[t4][ks]), acc[t4]);
+                    }
+                }
+                // acc[t4][e]: token row 4g + e of tile q, column grp + t4
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u32x2 yy = yv[q][e];
+                    const float r0 = bf16_bits_to_float(yy[0] & 0xffffu) + (acc[0][e] + bias[0]);
+                    const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][e] + bias[1]);
+                    const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][e] + bias[2]);
+                    const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][e] + bias[3]);
+                    *reinterpret_cast<u32x2 *>(a.y + (int64_t)ytok[q][e] * a.ldy + ycol) =
+                        u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                              pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
+                }
+            }
+        }
+        __syncthreads();   // the staged rows are rewritten by the next unit
     }
 }
 
@@ -234,9 +234,9 @@ ExpandFn pick_tt(int tt, bool add) {
 
 }  // namespace
 
-// Launch geometry from host-known sizes only: 256 columns per workgroup,
-// 16-token tiles per unit bounded by registers (TT * ceil(r/32) <= 4) and by
-// the expected segment length N / min(N, max_loras + 1).
+// Launch geometry from host-known sizes only: 256 columns per workgroup and
+// TT tiles of 16 tokens per unit, following the expected segment length
+// N / min(N, max_loras + 1).
 hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStream_t s) {
     ExpandArgs a = in;
     int blocks = 0;
@@ -250,7 +250,7 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     const int nslots = a.meta.nslots;
     const int segs = nslots < n ? nslots : n;
     const int ks = (a.rank + 31) / 32;
-    int tt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : 4 / ks;
+    int tt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : 4;
     if (cfg.tile_tokens <= 0) {
         const int avg = (n + segs - 1) / segs;
         while (tt > 1 && 16 * tt / 2 >= avg) tt /= 2;
@@ -271,7 +271,8 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
         case 3: fn = pick_tt<3>(tt, add); break;
         default: fn = pick_tt<4>(tt, add); break;
     }
-    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1);
+    a.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
+    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

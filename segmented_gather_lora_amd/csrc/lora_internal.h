@@ -81,8 +81,10 @@ struct MetaView {
     const int32_t *start_loc;    // [max_loras + 2]
     const int32_t *no_lora;      // [1]
     int32_t nslots;              // max_loras + 1
+    int32_t lds_tokens;          // > 0: the first lds_tokens sorted indices are copied to LDS
 };
 
+constexpr int kLdsTokensMax = 2048;   // batches up to this size keep sorted indices in LDS
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 // Per-workgroup table of work tiles, built in LDS from the metadata: every
@@ -93,10 +95,18 @@ constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robi
 // All threads of the block must call it; returns the total number of tiles.
 __device__ __forceinline__ int tile_table_ints(int nslots) { return 4 * nslots + 1; }
 
+// Sorted token index `idx`: from the LDS copy made by build_tile_table when
+// the batch is small (one memory round trip less per work unit), else HBM.
+__device__ __forceinline__ int sorted_at(const MetaView &m, const int *smem, int idx) {
+    return m.lds_tokens > 0 ? smem[4 * m.nslots + 1 + idx] : m.sorted[idx];
+}
+
 __device__ __forceinline__ int build_tile_table(const MetaView &m, int tile_tokens, int *smem, int *s_wsum) {
     const int nslots = m.nslots;
     int *pre = smem, *sid = smem + nslots + 1, *sst = sid + nslots, *scn = sst + nslots;
     const int nthreads = blockDim.x, tid = threadIdx.x;
+    // the sorted indices of a small batch come along in the same round trip
+    for (int k = tid; k < m.lds_tokens; k += nthreads) smem[4 * nslots + 1 + k] = m.sorted[k];
     const int per = (nslots + nthreads - 1) / nthreads;
     const int beg = tid * per;
     int sum = 0;
@@ -238,6 +248,8 @@ struct ShrinkTuning {
     int mtiles_per_wave;   // 1..4
     int k_splits;
     int grid_cap;
+    int variant;           // 2 = direct-load kernel, 3 = LDS-staged kernel
+    int staged_cfg;        // 1-based index into the LDS-staged configurations
 };
 struct ExpandTuning {
     int tile_tokens;       // 16, 32 or 64

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
             const int p = tr.tile * kTileTokens + nt * 16 + col;
             tv[nt] = p < tr.seg_count;
-            int t = a.meta.sorted[tr.seg_start + (tv[nt] ? p : tr.seg_count - 1)];
+            int t = sorted_at(a.meta, smem, tr.seg_start + (tv[nt] ? p : tr.seg_count - 1));
             if ((unsigned)t >= (unsigned)a.num_tokens) {   // metadata not from this batch
                 t = 0;
                 tv[nt] = false;
@@ -219,6 +219,195 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged variant for tiles of many tokens (prefill-like segments).
+//
+// A workgroup computes a tile of BT = 16*NT tokens x BR = 16*MR weight rows
+// over its K range.  Every 64-wide K step, the tile's BT token rows and BR
+// weight rows (128 bytes each) are copied from HBM straight into LDS with
+// global_load_lds_dwordx4: 8 lanes cover one row's 128 bytes, so each wave
+// instruction moves 8 whole row segments (1 KB, fully coalesced), and every
+// element is fetched once per workgroup.  The 16-byte chunks of row r are
+// stored XOR-swizzled (chunk c at slot c ^ (r & 7)) so that the MFMA operand
+// reads (ds_read_b128 of one chunk from 8 different rows) hit 8 different
+// bank groups.  STAGES steps are in flight; a wave waits only for the step it
+// is about to use (s_waitcnt vmcnt), then a barrier publishes the step to the
+// whole workgroup.  Waves split the tile as WR row groups x (4 / WR) token
+// groups; each output element belongs to one wave, so K chunks are combined
+// only across workgroups (float atomics), never inside one.
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// 16-byte LDS read issued as an opaque instruction: the stage protocol
+// (s_waitcnt vmcnt + barrier) already orders it after the direct-to-LDS
+// loads that filled the stage, and the compiler would otherwise wait for
+// every load in flight before each read.  Callers wait with lds_wait().
+__device__ __forceinline__ u32x4 lds_read16(const unsigned char *p) {
+    u32x4 r;
+    const uint32_t addr = (uint32_t)(uintptr_t)p;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Ties a register to the preceding lds_wait(): its consumers cannot be
+// scheduled above the wait (the value is an output of this statement).
+__device__ __forceinline__ void after_wait(u32x4 &v) { asm volatile("" : "+v"(v)); }
+
+template <int NT, int MR, int WR, int STAGES>
+__global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
+    constexpr int WC = 4 / WR;
+    constexpr int BT = 16 * NT, BR = 16 * MR, ROWS = BT + BR;
+    constexpr int INSTR = ROWS / 32;     // load instructions per wave per step
+    constexpr int MT = MR / WR, NTW = NT / WC;
+    static_assert(ROWS % 32 == 0 && MR % WR == 0 && NT % WC == 0, "tile shape");
+    extern __shared__ int smem[];
+    __shared__ int s_wsum[kThreads / kWave];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage[STAGES][ROWS * 128];
+
+    if (*a.meta.no_lora) return;
+    const int nslots = a.meta.nslots;
+    const int total = build_tile_table(a.meta, BT, smem, s_wsum);
+
+    const int lane = lane_id(), wave = wave_id();
+    const int wr = wave % WR, wc = wave / WR;
+    const int n16 = lane & 15, g = lane >> 4;
+    const bool atomic = a.k_splits > 1;
+
+    const UnitWalker walk(total * a.row_blocks * a.k_splits);
+    for (int jj = walk.first;; jj += walk.stride) {
+        const int u = walk.unit(jj);
+        if (u < 0) break;
+        const int ks = u % a.k_splits;
+        const int rest = u / a.k_splits;
+        const int rb = rest % a.row_blocks;
+        const TileRef tr = lookup_tile(smem, nslots, rest / a.row_blocks);
+        const int kbeg = ks * a.k_chunk;
+        const int kend = min(kbeg + a.k_chunk, a.hidden);
+        const int nsteps = (kend - kbeg + 63) / 64;
+
+        // this lane's source rows: instruction j covers tile rows (wave*INSTR + j)*8 .. +8
+        const uint16_t *src[INSTR];
+        int chunk_k[INSTR];
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int r = (wave * INSTR + j) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);       // global chunk landing in slot lane&7
+            chunk_k[j] = 8 * c;
+            if (r < BT) {
+                int p = tr.tile * BT + r;
+                p = p < tr.seg_count ? p : tr.seg_count - 1;
+                int t = a.meta.sorted[tr.seg_start + p];
+                t = (unsigned)t < (unsigned)a.num_tokens ? t : 0;
+                src[j] = a.x + (int64_t)t * a.ldx;
+            } else {
+                int row = rb * BR + (r - BT);
+                row = row < a.rows ? row : a.rows - 1;
+                const int i = row / a.rank, jr = row - i * a.rank;
+                src[j] = select_ptr(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
+            }
+        }
+        auto issue = [&](int step, int buf) {
+            const int sc = step < nsteps ? step : nsteps - 1;   // past the end: reload, never skip
+#pragma unroll
+            for (int j = 0; j < INSTR; ++j) {
+                const int k = kbeg + sc * 64 + chunk_k[j];
+                const uint16_t *gp = src[j] + (k + 8 <= kend ? k : 0);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gp),
+                                                 reinterpret_cast<void *>(&stage[buf][(wave * INSTR + j) * 1024]),
+                                                 16, 0, 0);
+            }
+        };
+
+        floatx4 acc[MT][NTW];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st) issue(st, st);
+
+        for (int s = 0; s < nsteps; ++s) {
+            issue(s + STAGES - 1, (s + STAGES - 1) % STAGES);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 1) * INSTR));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            const unsigned char *sb = stage[s % STAGES];
+            const bool mask = s == nsteps - 1 && ((kend - kbeg) & 63) != 0;
+            u32x4 xa[2][NTW], wa[2][MT];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 2 * g + h;
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const int r = (wc * NTW + nt) * 16 + n16;
+                    xa[h][nt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int r = BT + (wr * MT + mt) * 16 + n16;
+                    wa[h][mt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
+                }
+            }
+            lds_wait();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) after_wait(xa[h][nt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) after_wait(wa[h][mt]);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (mask && kbeg + s * 64 + 8 * (2 * g + h) + 8 > kend) {
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) xa[h][nt] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) wa[h][mt] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        acc[mt][nt] = mfma16x16x32(as_bf16x8(wa[h][mt]), as_bf16x8(xa[h][nt]), acc[mt][nt]);
+            }
+            __builtin_amdgcn_s_barrier();   // every wave has read the stage: it may be refilled
+        }
+        // drain the dummy loads issued past the end before the stages are reused
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+
+        // D layout: lane holds rows 4g..4g+3 of m-tile mt for token column n16 of n-tile nt
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = tr.tile * BT + (wc * NTW + nt) * 16 + n16;
+            if (p >= tr.seg_count) continue;
+            int t = a.meta.sorted[tr.seg_start + p];
+            if ((unsigned)t >= (unsigned)a.num_tokens) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row0 = rb * BR + (wr * MT + mt) * 16 + 4 * g;
+                if (row0 >= a.rows) continue;
+                const int i = row0 / a.rank, jr = row0 - i * a.rank;
+                float *dst = a.buf + ((int64_t)i * a.num_tokens + t) * a.rank + jr;
+                const floatx4 v = acc[mt][nt] * a.scale;
+                if (atomic) {
+                    unsafeAtomicAdd(dst + 0, v[0]);
+                    unsafeAtomicAdd(dst + 1, v[1]);
+                    unsafeAtomicAdd(dst + 2, v[2]);
+                    unsafeAtomicAdd(dst + 3, v[3]);
+                } else {
+                    floatx4 o = *reinterpret_cast<floatx4 *>(dst);
+                    o += v;
+                    *reinterpret_cast<floatx4 *>(dst) = o;
+                }
+            }
+        }
+    }
+}
+
 typedef void (*ShrinkFn)(ShrinkArgs);
 
 template <int NT, int WK>
@@ -249,12 +438,36 @@ ShrinkFn pick(int nt, int wk, int mt) {
     }
 }
 
+
+// LDS-staged configurations: tokens x rows per workgroup, wave layout, stages.
+struct StagedCfg {
+    int nt, mr, wr, stages;
+    bool automatic;   // eligible for the automatic choice
+    ShrinkFn fn;
+};
+const StagedCfg kStaged[] = {
+    {4, 12, 4, 3, true, shrink_lds_kernel<4, 12, 4, 3>},    // 0: 64 tokens x 192 rows
+    {8, 12, 4, 3, false, shrink_lds_kernel<8, 12, 4, 3>},   // 1: 128 x 192 (one wave per SIMD: slow)
+    {4, 8, 4, 4, true, shrink_lds_kernel<4, 8, 4, 4>},      // 2: 64 x 128
+    {4, 4, 4, 4, true, shrink_lds_kernel<4, 4, 4, 4>},      // 3: 64 x 64
+    {4, 2, 2, 4, true, shrink_lds_kernel<4, 2, 2, 4>},      // 4: 64 x 32
+    {2, 12, 4, 4, true, shrink_lds_kernel<2, 12, 4, 4>},    // 5: 32 x 192
+    {8, 4, 4, 4, true, shrink_lds_kernel<8, 4, 4, 4>},      // 6: 128 x 64
+    {8, 2, 2, 4, true, shrink_lds_kernel<8, 2, 2, 4>},      // 7: 128 x 32
+    {2, 4, 4, 4, true, shrink_lds_kernel<2, 4, 4, 4>},      // 8: 32 x 64
+    {2, 2, 2, 4, true, shrink_lds_kernel<2, 2, 2, 4>},      // 9: 32 x 32
+    {4, 6, 2, 5, true, shrink_lds_kernel<4, 6, 2, 5>},      // 10: 64 x 96
+    {8, 6, 2, 4, true, shrink_lds_kernel<8, 6, 2, 4>},      // 11: 128 x 96
+};
+constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
+
 }  // namespace
 
-// Tile selection from host-known sizes only (no device sync): tokens per
-// tile follow the expected segment length N / min(N, max_loras + 1); rows
-// are split over the 4 waves when there are enough 16-row MFMA tiles, else
-// K is interleaved over the waves; K chunks are added only when the units
+// Tile selection from host-known sizes only (no device sync).  The expected
+// segment length N / min(N, max_loras + 1) picks the kernel: short segments
+// (decode-like) use the direct-load kernel with K interleaved over the waves,
+// long ones the LDS-staged kernel with a tile of 64-128 tokens x up to 192
+// rows.  K chunks (combined with float atomics) are added only when the units
 // would not cover the GPU.  `cfg` fields > 0 override the choice (tuning).
 hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStream_t s) {
     ShrinkArgs a = in;
@@ -263,26 +476,69 @@ hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStrea
     const int mtiles = (a.rows + 15) / 16;
     const int segs = nslots < n ? nslots : n;
     const int avg = (n + segs - 1) / segs;
+    const int max_ks = (a.hidden + 255) / 256;
 
-    int nt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : (avg <= 16 ? 1 : (avg <= 32 ? 2 : (avg <= 64 ? 4 : 8)));
-    if (nt != 1 && nt != 2 && nt != 4) nt = 8;
-    int wk = cfg.waves_k;
-    if (wk != 1 && wk != 2 && wk != 4) wk = mtiles >= 8 ? 1 : (mtiles >= 4 ? 2 : 4);
-    const int wr = 4 / wk;
-    int mt = cfg.mtiles_per_wave > 0 ? cfg.mtiles_per_wave : (mtiles + wr - 1) / wr;
-    if (mt > 4) mt = 4;
-    if (nt == 8 && mt > 2) mt = 2;
-    const int rows_per_wg = wr * mt * 16;
+    bool staged = cfg.variant == 3 || (cfg.variant == 0 && avg >= 24);
+    int tile_tokens, rows_per_wg;
+    int forced_ks = cfg.k_splits;
+    ShrinkFn fn;
+    if (staged) {
+        int idx = cfg.staged_cfg;
+        if (idx <= 0 || idx > kNumStaged) {
+            // Cost model: a unit streams (tokens + rows) x K_chunk bf16 through
+            // LDS at about the same rate on every CU, so the time goes as
+            // max(units / CUs, 1) x bytes per unit; every extra K chunk adds
+            // one float atomic per active (token, row) element.
+            const double cus = 256.0, bytes_per_atomic = 100.0;   // fitted to measured split-K cost
+            double best = 1e300;
+            for (int c = 0; c < kNumStaged; ++c) {
+                if (!kStaged[c].automatic) continue;
+                const int T = 16 * kStaged[c].nt, R = 16 * kStaged[c].mr;
+                const double tiles = (double)segs * ((avg + T - 1) / T);
+                const double rb = (a.rows + R - 1) / R;
+                for (int ksc = 1; ksc <= 4; ksc *= 2) {
+                    if (forced_ks > 0 && ksc != forced_ks) continue;
+                    const double units = tiles * rb * ksc;
+                    const double per_unit = (double)(T + R) * 2.0 * ((a.hidden + ksc - 1) / ksc);
+                    double cost = (units / cus > 1.0 ? units / cus : 1.0) * per_unit;
+                    // waste on rows past S*r and tokens past the segment end
+                    cost *= (rb * R) / (double)a.rows;
+                    if (ksc > 1) cost += ksc * (double)n * a.rows * bytes_per_atomic / cus;
+                    if (cost < best) {
+                        best = cost;
+                        idx = c;
+                        if (forced_ks <= 0) a.k_splits = ksc;
+                    }
+                }
+            }
+            if (forced_ks <= 0) forced_ks = a.k_splits;
+        } else {
+            idx -= 1;
+        }
+        const StagedCfg &c = kStaged[idx];
+        tile_tokens = 16 * c.nt;
+        rows_per_wg = 16 * c.mr;
+        fn = c.fn;
+    } else {
+        int nt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : (avg <= 16 ? 1 : (avg <= 32 ? 2 : 4));
+        if (nt != 1 && nt != 2 && nt != 4) nt = 8;
+        int wk = cfg.waves_k;
+        if (wk != 1 && wk != 2 && wk != 4) wk = mtiles >= 8 ? 1 : (mtiles >= 4 ? 2 : 4);
+        const int wr = 4 / wk;
+        int mt = cfg.mtiles_per_wave > 0 ? cfg.mtiles_per_wave : (mtiles + wr - 1) / wr;
+        if (mt > 4) mt = 4;
+        if (nt == 8 && mt > 2) mt = 2;
+        tile_tokens = 16 * nt;
+        rows_per_wg = wr * mt * 16;
+        fn = pick(nt, wk, mt);
+    }
     a.row_blocks = (a.rows + rows_per_wg - 1) / rows_per_wg;
 
-    const int tile_tokens = 16 * nt;
     const int tiles_upper = (n + tile_tokens - 1) / tile_tokens + segs;
     const int busy = ((n + tile_tokens - 1) / tile_tokens + (segs + 1) / 2) * a.row_blocks;
     int ks = 1;
-    const int target = 2 * 256;
-    if (busy < target) ks = (target + busy - 1) / busy;
-    const int max_ks = (a.hidden + 255) / 256;
-    if (cfg.k_splits > 0) ks = cfg.k_splits;
+    if (!staged && busy < 256) ks = (256 + busy - 1) / busy;
+    if (forced_ks > 0) ks = forced_ks;
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
     int chunk = (a.hidden + ks - 1) / ks;
@@ -291,13 +547,14 @@ hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStrea
     a.k_splits = ks;
     a.k_chunk = chunk;
     const long units_upper = (long)tiles_upper * a.row_blocks * ks;
-    const int cap = cfg.grid_cap > 0 ? cfg.grid_cap : 1024;
+    const int cap = cfg.grid_cap > 0 ? cfg.grid_cap : (staged ? 512 : 1024);
     long grid = units_upper < cap ? units_upper : cap;
     grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
     a.num_units = (int)units_upper;
 
-    ShrinkFn fn = pick(nt, wk, mt);
-    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1);
+    // small batches: the direct-load kernel keeps the sorted indices in LDS
+    a.meta.lds_tokens = (!staged && n <= kLdsTokensMax) ? n : 0;
+    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

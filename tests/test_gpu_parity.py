@@ -187,6 +187,7 @@ def test_offset_start_and_wide_rows():
 @pytest.mark.parametrize("tile,wk,ks", [(16, 1, 1), (16, 2, 3), (16, 4, 1), (32, 1, 2), (32, 2, 1),
                                         (32, 4, 4), (64, 1, 1), (64, 2, 2), (64, 4, 3)])
 def test_shrink_tile_variants(tile, wk, ks, monkeypatch):
+    monkeypatch.setenv("LORA_SHRINK_VARIANT", "2")
     monkeypatch.setenv("LORA_SHRINK_TILE_TOKENS", str(tile))
     monkeypatch.setenv("LORA_SHRINK_WAVES_K", str(wk))
     monkeypatch.setenv("LORA_SHRINK_KSPLIT", str(ks))
@@ -299,3 +300,23 @@ def test_invalid_arguments_raise():
     assert e.value.status == sgl.LORA_ERR_SHAPE
     with pytest.raises(sgl.LoraError):
         sgl.lora_prepare_meta(torch.zeros(9, dtype=torch.int32, device="cuda"), meta)
+
+
+@pytest.mark.parametrize("cfg", range(1, 13))
+@pytest.mark.parametrize("ks", [1, 3])
+def test_shrink_staged_variants(cfg, ks, monkeypatch):
+    """Every LDS-staged shrink configuration on a ragged case: K not a
+    multiple of 64, rows not a multiple of the row block, short segments."""
+    monkeypatch.setenv("LORA_SHRINK_VARIANT", "3")
+    monkeypatch.setenv("LORA_SHRINK_STAGED", str(cfg))
+    monkeypatch.setenv("LORA_SHRINK_KSPLIT", str(ks))
+    wl = workloads.random_case(200 + cfg, 517, 712, (72, 40, 104), 8, 6, bias=True, neg_fraction=0.15)
+    print("staged shrink", cfg, ks, flush=True)
+    H.run_and_check(wl, add_inputs=True)
+
+
+def test_shrink_staged_full_rows(monkeypatch):
+    """Staged kernel with 3 slices of rank 64 (192 rows), one long segment."""
+    monkeypatch.setenv("LORA_SHRINK_VARIANT", "3")
+    wl = workloads.random_case(230, 1000, 1024, (128, 64, 64), 64, 2, neg_fraction=0.0)
+    H.run_and_check(wl, add_inputs=True)
