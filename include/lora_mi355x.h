@@ -51,6 +51,7 @@ typedef enum lora_status {
 #define LORA_MAX_LORAS 1023      /* ids 0 .. 1022; -1 = no LoRA */
 #define LORA_MAX_SLICES 8
 #define LORA_MAX_RANK 128
+#define LORA_MAX_TOKENS 2097152  /* tokens per batch */
 
 /*
  * Per-batch kernel metadata (LoRAKernelMeta on the "lora_kernel_metadata"
@@ -93,14 +94,17 @@ size_t lora_meta_bytes(int max_loras, int max_num_tokens);
  * is done: the arrays hold garbage until the first lora_prepare_meta().
  * host_no_lora is set to NULL; the caller may point it at pinned host memory. */
 int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out);
+/* (max_num_tokens above LORA_MAX_TOKENS is rejected with LORA_ERR_NUM_TOKENS.) */
 
 /*
  * LoRAKernelMeta._reset + prepare_tensors for one batch
  * ("lora_kernel_metadata" page).  mapping: int32[num_tokens] token -> LoRA id
  * (-1 = none), device memory.  On device, in one launch:
  *   reset active ids to -1, counts and start_loc to 0; set no_lora_flag to
- *   all(mapping == -1); if set, stop there (mapping copy and sorted indices
- *   are left as they were, as the pages' early return does); otherwise copy
+ *   all(mapping == -1); if set, stop there (the sorted indices are left as
+ *   they were, as the pages' early return does, and so is the mapping copy
+ *   for batches of up to 16384 tokens; larger batches use it as scratch);
+ *   otherwise copy
  *   the mapping, stable-sort token indices by id (ascending, ties in token
  *   order), write the distinct ids with their counts, and the segment starts.
  * Ids outside [-1, max_loras) are treated as -1 and reported in meta->status.

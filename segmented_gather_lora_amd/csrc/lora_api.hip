@@ -40,7 +40,7 @@ int check_meta(const lora_meta_t *m) {
         !m->num_tokens_per_lora || !m->lora_token_start_loc || !m->no_lora_flag || !m->status)
         return LORA_ERR_NULL;
     if (m->max_loras < 1 || m->max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
-    if (m->max_num_tokens < 0) return LORA_ERR_NUM_TOKENS;
+    if (m->max_num_tokens < 0 || m->max_num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
     return LORA_OK;
 }
 
@@ -49,7 +49,8 @@ int check_meta(const lora_meta_t *m) {
 extern "C" {
 
 size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
-    if (max_loras < 1 || max_loras > LORA_MAX_LORAS || max_num_tokens < 0) return 0;
+    if (max_loras < 1 || max_loras > LORA_MAX_LORAS || max_num_tokens < 0 || max_num_tokens > LORA_MAX_TOKENS)
+        return 0;
     const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
     return 2 * tok + 2 * round_up(sizeof(int32_t) * (max_loras + 1)) +
            round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign;
@@ -58,7 +59,7 @@ size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
 int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out) {
     if (!dev || !out) return LORA_ERR_NULL;
     if (max_loras < 1 || max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
-    if (max_num_tokens < 0) return LORA_ERR_NUM_TOKENS;
+    if (max_num_tokens < 0 || max_num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
     if ((reinterpret_cast<uintptr_t>(dev) & (kAlign - 1)) != 0) return LORA_ERR_BUFFER;
     const size_t need = lora_meta_bytes(max_loras, max_num_tokens);
     if (bytes < need) return LORA_ERR_BUFFER;

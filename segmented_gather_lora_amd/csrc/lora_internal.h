@@ -40,13 +40,17 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
     return m;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane moves:
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of a
+// row is broadcast into the next row (row_bcast:15) and the last lane of row 1
+// into rows 2 and 3 (row_bcast:31).  Lanes without a source add 0.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int o = __shfl_up(v, d, kWave);
-        if (lane_id() >= d) v += o;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
     return v;
 }
 

@@ -5,16 +5,24 @@
 // stable sort of token indices by id, the ascending distinct ids with their
 // counts (torch.unique(sorted=True, return_counts=True)) and their running
 // sums (torch.cumsum) shifted by one slot.  The sort is a counting sort over
-// the <= 1024 keys (id + 1), so it is stable and bit-exact by construction:
+// the <= 1024 keys (key = id + 1), stable and bit-exact by construction.
 //
-//   pass 1: histogram of keys; each wave groups equal keys with one ballot
-//           per key bit, and one lane per group adds the group size (LDS).
-//   scan:   one thread per key; block-wide exclusive scans give each
-//           non-empty key its slot and its first sorted position.
-//   pass 2: tiles of 1024 tokens in order; a token's position is its key's
-//           running cursor + the count of equal keys in earlier waves of the
-//           tile (per-wave table in LDS) + its rank among equal keys of its
-//           own wave (popcount of the match mask below its lane).
+// The batch is cut into 16 contiguous slices, one per wave, so a token's
+// sorted position is
+//   start[key] + sum over earlier slices of count[slice][key]
+//              + number of equal keys before it in its own slice.
+//   1. Each wave walks its slice 64 tokens at a time with no barrier: the
+//      equal keys of a step are grouped with one ballot per key bit (match
+//      mask), a token's rank in the slice is the slice's running count of its
+//      key plus the popcount of the match mask below its lane, and one lane
+//      per group bumps the running count (an LDS column owned by the wave).
+//   2. One thread per key adds up its 16 slice counts (the histogram), a
+//      block scan over the keys gives the segment starts and the compacted
+//      id list, and each key's 16 counts become 16 slice bases.
+//   3. Every token is written to base[key][slice] + rank.
+// A slice's keys are loaded in one batch and kept in registers with their
+// ranks when the slice has at most kSteps steps of 64 tokens; longer slices
+// park (key, rank) in the mapping-copy array between steps 1 and 3.
 #include "lora_internal.h"
 
 namespace lora {
@@ -24,68 +32,71 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxKeys = LORA_MAX_LORAS + 1;
-
-// Block-wide exclusive scan of two values; returns the totals too.
-__device__ __forceinline__ void block_scan2(int a, int b, int &ea, int &eb, int &ta, int &tb,
-                                            int *s_wa, int *s_wb) {
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    int ia = wave_inclusive_scan(a);
-    int ib = wave_inclusive_scan(b);
-    if (lane == kWave - 1) {
-        s_wa[wave] = ia;
-        s_wb[wave] = ib;
-    }
-    __syncthreads();
-    int pa = 0, pb = 0;
-    ta = 0;
-    tb = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        int va = s_wa[w], vb = s_wb[w];
-        if (w < wave) {
-            pa += va;
-            pb += vb;
-        }
-        ta += va;
-        tb += vb;
-    }
-    ea = pa + ia - a;
-    eb = pb + ib - b;
-}
+constexpr int kSteps = 16;     // steps of 64 tokens per wave held in registers
+constexpr int kRankBits = 21;  // (key << 21) | rank: keys < 1024, ranks < 2^21 tokens
+constexpr int kRankMask = (1 << kRankBits) - 1;
 
 __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
-    __shared__ int s_cnt[kMaxKeys];
-    __shared__ int s_cur[kMaxKeys];
-    __shared__ uint16_t s_wt[kWaves][kMaxKeys];
+    // per key: the running count of each wave's slice (later its base)
+    __shared__ __attribute__((aligned(16))) int s_cnt[kMaxKeys][kWaves];
     __shared__ int s_wa[kWaves], s_wb[kWaves];
     __shared__ int s_any, s_bad;
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int n = a.num_tokens;
     const int nkeys = a.max_loras + 1;
     const int nbits = 32 - __clz(nkeys - 1);   // keys 0 .. nkeys-1 fit in nbits
+    const int steps = (n + kThreads - 1) / kThreads;   // 64-token steps per wave
+    const int slice = steps * kWave;                    // tokens per wave
+    const int t0 = wave * slice;
+    const bool in_regs = steps <= kSteps;
 
-    for (int k = tid; k < nkeys; k += kThreads) s_cnt[k] = 0;
-    for (int k = tid; k < kWaves * kMaxKeys; k += kThreads) (&s_wt[0][0])[k] = 0;
+    {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int k = tid; k < nkeys * (kWaves / 4); k += kThreads)
+            reinterpret_cast<u32x4 *>(&s_cnt[0][0])[k] = z;
+    }
     if (tid == 0) {
         s_any = 0;
         s_bad = 0;
     }
     __syncthreads();
 
-    // ---- pass 1: histogram, any-active, bad ids
+    // ---- 1. ranks within the wave's slice
+    int packed[kSteps];
     bool any = false, bad = false;
-    for (int base = 0; base < n; base += kThreads) {
-        const int t = base + tid;
-        const bool valid = t < n;
-        int id = valid ? a.mapping[t] : -1;
-        if (id < -1 || id >= a.max_loras) {
-            bad = true;
-            id = -1;
+    for (int c0 = 0; c0 < steps; c0 += kSteps) {
+        int ids[kSteps];
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {   // one round trip for the chunk (addresses clamped)
+            const int t = t0 + (c0 + q) * kWave + lane;
+            ids[q] = a.mapping[t < n ? t : n - 1];
         }
-        const int key = id + 1;
-        any |= valid && id != -1;
-        const uint64_t m = match_key(key, valid, nbits);
-        if (valid && (m & lanemask_lt()) == 0) atomicAdd(&s_cnt[key], __popcll(m));
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            if (c0 + q >= steps) break;   // uniform
+            const int t = t0 + (c0 + q) * kWave + lane;
+            const bool valid = t < n;
+            int id = valid ? ids[q] : -1;
+            if (id < -1 || id >= a.max_loras) {
+                bad = true;
+                id = -1;
+            }
+            const int key = id + 1;
+            any |= valid && id != -1;
+            const uint64_t m = match_key(key, valid, nbits);
+            const bool leader = valid && (m & lanemask_lt()) == 0;
+            const int rank = s_cnt[key][wave] + __popcll(m & lanemask_lt());
+            packed[q] = (key << kRankBits) | rank;
+            if (leader) s_cnt[key][wave] += __popcll(m);   // this wave's column only
+        }
+        if (!in_regs) {
+#pragma unroll
+            for (int q = 0; q < kSteps; ++q) {
+                const int t = t0 + (c0 + q) * kWave + lane;
+                if (c0 + q < steps && t < n) a.mapping_copy[t] = packed[q];
+            }
+        }
     }
     if (ballot(any) && lane == 0) atomicOr(&s_any, 1);
     if (ballot(bad) && lane == 0) atomicOr(&s_bad, 1);
@@ -97,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
         *a.status = s_bad ? LORA_ERR_ID_RANGE : 0;
     }
     if (no_lora) {
-        // _reset values, then the pages' early return
+        // _reset values, then the pages' early return (sorted indices untouched;
+        // the mapping copy too unless it served as scratch for a long batch)
         for (int k = tid; k < nkeys; k += kThreads) {
             a.active_ids[k] = -1;
             a.counts[k] = 0;
@@ -106,17 +118,54 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
         return;
     }
 
-    // ---- scan over keys (nkeys <= kThreads: one key per thread)
-    const int c = tid < nkeys ? s_cnt[tid] : 0;
+    // ---- 2. histogram, scan over keys (nkeys <= kThreads: one key per thread), slice bases
+    int col[kWaves];
+    int c = 0;
+    if (tid < nkeys) {
+#pragma unroll
+        for (int v = 0; v < kWaves / 4; ++v) {
+            const u32x4 q4 = reinterpret_cast<const u32x4 *>(&s_cnt[tid][0])[v];
+            col[4 * v] = (int)q4[0];
+            col[4 * v + 1] = (int)q4[1];
+            col[4 * v + 2] = (int)q4[2];
+            col[4 * v + 3] = (int)q4[3];
+        }
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += col[w];
+    }
     const int ne = c > 0 ? 1 : 0;
-    int start, slot, total, n_active;
-    block_scan2(c, ne, start, slot, total, n_active, s_wa, s_wb);
+    const int ic = wave_inclusive_scan(c), ine = wave_inclusive_scan(ne);
+    if (lane == kWave - 1) {
+        s_wa[wave] = ic;
+        s_wb[wave] = ine;
+    }
+    __syncthreads();
+    int start = ic - c, slot = ine - ne, n_active = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int va = s_wa[w], vb = s_wb[w];
+        start += w < wave ? va : 0;
+        slot += w < wave ? vb : 0;
+        n_active += vb;
+    }
     if (ne) {
         a.active_ids[slot] = tid - 1;
         a.counts[slot] = c;
         a.start_loc[slot + 1] = start + c;
     }
-    if (tid < nkeys) s_cur[tid] = start;
+    if (tid < nkeys) {
+        int run = start;
+#pragma unroll
+        for (int v = 0; v < kWaves / 4; ++v) {
+            u32x4 q4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                q4[e] = (uint32_t)run;
+                run += col[4 * v + e];
+            }
+            reinterpret_cast<u32x4 *>(&s_cnt[tid][0])[v] = q4;
+        }
+    }
     for (int k = tid; k < nkeys; k += kThreads) {
         if (k >= n_active) {
             a.active_ids[k] = -1;
@@ -127,30 +176,29 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
         if (k == 0 || k > n_active) a.start_loc[k] = 0;
     __syncthreads();
 
-    // ---- pass 2: stable scatter, tile by tile
-    for (int base = 0; base < n; base += kThreads) {
-        const int t = base + tid;
-        const bool valid = t < n;
-        int id = valid ? a.mapping[t] : -1;
-        if (id < -1 || id >= a.max_loras) id = -1;
-        const int key = id + 1;
-        const uint64_t m = match_key(key, valid, nbits);
-        const bool leader = valid && (m & lanemask_lt()) == 0;
-        const int rank = __popcll(m & lanemask_lt());
-        if (leader) s_wt[wave][key] = (uint16_t)__popcll(m);
-        __syncthreads();
-        if (valid) {
-            int pos = s_cur[key] + rank;
-            for (int w = 0; w < wave; ++w) pos += s_wt[w][key];
-            if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
-            a.mapping_copy[t] = id;
+    // ---- 3. stable scatter
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            const int t = t0 + q * kWave + lane;
+            if (q < steps && t < n) {
+                const int key = (int)((unsigned)packed[q] >> kRankBits), rank = packed[q] & kRankMask;
+                const int pos = s_cnt[key][wave] + rank;
+                if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
+                a.mapping_copy[t] = key - 1;
+            }
         }
-        __syncthreads();
-        if (leader) {
-            atomicAdd(&s_cur[key], __popcll(m));
-            s_wt[wave][key] = 0;
+    } else {
+        for (int s = 0; s < steps; ++s) {
+            const int t = t0 + s * kWave + lane;
+            if (t < n) {
+                const int v = a.mapping_copy[t];
+                const int key = (int)((unsigned)v >> kRankBits), rank = v & kRankMask;
+                const int pos = s_cnt[key][wave] + rank;
+                if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
+                a.mapping_copy[t] = key - 1;
+            }
         }
-        // the next tile's first barrier orders these updates before any read
     }
 }
 

@@ -46,7 +46,8 @@ def test_prepare_workload_mappings(name):
 @pytest.mark.parametrize("seed,n,ml,neg", [
     (1, 1, 1, 0.0), (2, 63, 3, 0.3), (3, 64, 3, 0.3), (4, 65, 7, 0.3), (5, 1023, 32, 0.1),
     (6, 1024, 32, 0.0), (7, 1025, 128, 0.2), (8, 5000, 1023, 0.2), (9, 20000, 64, 0.05),
-    (10, 3000, 1, 0.5), (11, 2049, 255, 0.0), (12, 777, 511, 0.9)])
+    (10, 3000, 1, 0.5), (11, 2049, 255, 0.0), (12, 777, 511, 0.9), (13, 70000, 1023, 0.1),
+    (14, 16384, 2, 0.0), (15, 16385, 1023, 0.5)])
 def test_prepare_random(seed, n, ml, neg):
     rng = np.random.default_rng(seed)
     m = rng.integers(0, ml, n).astype(np.int32)
