@@ -63,9 +63,8 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_hi[kUnitTokens * kRowStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_lo[kUnitTokens * kRowStride];
 
-    if (*a.meta.no_lora) return;
     const int nslots = a.meta.nslots;
-    const int total = build_tile_table(a.meta, kUnitTokens, smem, s_wsum);
+    const int total = build_tile_table<kThreads>(a.meta, kUnitTokens, smem, s_wsum);
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int n16 = lane & 15, g = lane >> 4;

@@ -96,7 +96,12 @@ constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robi
 // (so no order of the segments is assumed).  Layout in `smem` (ints):
 //   pre[nslots + 1]  exclusive prefix of tiles per slot (pre[nslots] = total)
 //   sid[nslots], sstart[nslots], scnt[nslots]
-// All threads of the block must call it; returns the total number of tiles.
+// followed, for batches of at most kLdsTokensMax tokens, by the sorted token
+// indices.  Every metadata read (the no-LoRA flag, ids, counts, segment
+// starts, sorted indices) is issued before any is used: the table costs one
+// memory round trip.  A batch flagged no-LoRA has no tiles (its reset
+// metadata has none either).  All NTHREADS threads of the block must call it;
+// returns the total number of tiles.
 __device__ __forceinline__ int tile_table_ints(int nslots) { return 4 * nslots + 1; }
 
 // Sorted token index `idx`: from the LDS copy made by build_tile_table when
@@ -105,44 +110,79 @@ __device__ __forceinline__ int sorted_at(const MetaView &m, const int *smem, int
     return m.lds_tokens > 0 ? smem[4 * m.nslots + 1 + idx] : m.sorted[idx];
 }
 
+template <int NTHREADS>
 __device__ __forceinline__ int build_tile_table(const MetaView &m, int tile_tokens, int *smem, int *s_wsum) {
+    constexpr int kPerMax = (LORA_MAX_LORAS + 1 + NTHREADS - 1) / NTHREADS;   // slots per thread
+    constexpr int kTokPer = (kLdsTokensMax + NTHREADS - 1) / NTHREADS;        // sorted indices per thread
+    constexpr int kWavesT = NTHREADS / kWave;
     const int nslots = m.nslots;
     int *pre = smem, *sid = smem + nslots + 1, *sst = sid + nslots, *scn = sst + nslots;
-    const int nthreads = blockDim.x, tid = threadIdx.x;
-    // the sorted indices of a small batch come along in the same round trip
-    for (int k = tid; k < m.lds_tokens; k += nthreads) smem[4 * nslots + 1 + k] = m.sorted[k];
-    const int per = (nslots + nthreads - 1) / nthreads;
+    const int tid = threadIdx.x;
+    const int per = (nslots + NTHREADS - 1) / NTHREADS;
     const int beg = tid * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-        const int k = beg + i;
-        if (k < nslots) {
-            const int id = m.active_ids[k], c = m.counts[k];
-            const int nt = id >= 0 ? (c + tile_tokens - 1) / tile_tokens : 0;
-            sid[k] = id;
-            scn[k] = c;
-            sst[k] = nt ? m.start_loc[k] : 0;
-            pre[k] = nt;   // temporarily the tile count
-            sum += nt;
+
+    // ---- all loads first (clamped addresses, no branches)
+    const int flag = *m.no_lora;
+    int ids[kPerMax], cnt[kPerMax], st[kPerMax];
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i) {
+        int k = beg + i;
+        k = k < nslots ? k : nslots - 1;
+        ids[i] = m.active_ids[k];
+        cnt[i] = m.counts[k];
+        st[i] = m.start_loc[k];
+    }
+    int tok[kTokPer];
+    const int ntok = m.lds_tokens;
+    if (ntok > 0) {
+#pragma unroll
+        for (int i = 0; i < kTokPer; ++i) {
+            int k = tid + i * NTHREADS;
+            k = k < ntok ? k : ntok - 1;
+            tok[i] = m.sorted[k];
         }
     }
-    const int lane = lane_id(), wave = tid / kWave, nwaves = nthreads / kWave;
+
+    // ---- LDS copies and the per-thread tile counts
+    if (ntok > 0) {
+#pragma unroll
+        for (int i = 0; i < kTokPer; ++i) {
+            const int k = tid + i * NTHREADS;
+            if (k < ntok) smem[4 * nslots + 1 + k] = tok[i];
+        }
+    }
+    int nt[kPerMax];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i) {
+        const int k = beg + i;
+        nt[i] = 0;
+        if (i < per && k < nslots) {
+            nt[i] = (flag == 0 && ids[i] >= 0) ? (cnt[i] + tile_tokens - 1) / tile_tokens : 0;
+            sid[k] = ids[i];
+            scn[k] = cnt[i];
+            sst[k] = nt[i] ? st[i] : 0;
+            sum += nt[i];
+        }
+    }
+    const int lane = lane_id(), wave = tid / kWave;
     const int incl = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s_wsum[wave] = incl;
     __syncthreads();
     int base = 0, total = 0;
-    for (int w = 0; w < nwaves; ++w) {
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) {
         const int v = s_wsum[w];
         base += w < wave ? v : 0;
         total += v;
     }
     int run = base + incl - sum;
-    for (int i = 0; i < per; ++i) {
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i) {
         const int k = beg + i;
-        if (k < nslots) {
-            const int nt = pre[k];
+        if (i < per && k < nslots) {
             pre[k] = run;
-            run += nt;
+            run += nt[i];
         }
     }
     if (tid == 0) pre[nslots] = total;
@@ -173,7 +213,8 @@ __device__ __forceinline__ TileRef lookup_tile(const int *smem, int nslots, int 
 }
 
 // Units are numbered in a canonical order (tile-major) and cut into kNumXcd
-// contiguous chunks; workgroup b (on XCD b % 8) walks chunk b % 8, so
+// contiguous chunks; workgroup b walks chunk b % 8.  Workgroups are dealt to
+// the XCDs round-robin, so all workgroups with the same b % 8 run on one XCD and
 // neighbouring units -- the tiles of one segment, or the row/column blocks of
 // one tile -- run on the same XCD and share its L2.
 struct UnitWalker {

@@ -76,9 +76,8 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
     __shared__ int s_wsum[kThreads / kWave];
     __shared__ floatx4 red[(WK > 1 ? WK - 1 : 1) * WR * MT * NT * kWave];
 
-    if (*a.meta.no_lora) return;
     const int nslots = a.meta.nslots;
-    const int total = build_tile_table(a.meta, kTileTokens, smem, s_wsum);
+    const int total = build_tile_table<kThreads>(a.meta, kTileTokens, smem, s_wsum);
 
     const int lane = lane_id(), wave = wave_id();
     const int wk = wave % WK, wr = wave / WK;
@@ -265,9 +264,8 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
     __shared__ int s_wsum[kThreads / kWave];
     __shared__ __attribute__((aligned(1024))) unsigned char stage[STAGES][ROWS * 128];
 
-    if (*a.meta.no_lora) return;
     const int nslots = a.meta.nslots;
-    const int total = build_tile_table(a.meta, BT, smem, s_wsum);
+    const int total = build_tile_table<kThreads>(a.meta, BT, smem, s_wsum);
 
     const int lane = lane_id(), wave = wave_id();
     const int wr = wave % WR, wc = wave / WR;
