@@ -47,7 +47,7 @@ def algorithmic_bytes(wl) -> dict:
     for L in wl.layers:
         sp = L.spec
         S, r, H, O = len(sp.slices), sp.rank, sp.hidden, sum(sp.slices)
-        out["shrink"].append(2 * ta * H + 2 * la * S * r * H + 8 * S * ta * r)
+        out["shrink"].append(0 if sp.expand_only else 2 * ta * H + 2 * la * S * r * H + 8 * S * ta * r)
         bias = 2 * la * O if L.bias is not None else 0
         out["expand"].append(4 * S * ta * r + 2 * la * r * O + bias + 2 * ta * O * 2)
     return out
@@ -82,8 +82,12 @@ class DeviceSet:
                 s = src.layers[li]
                 d = dict(x=s["x"].clone(), a=[t.clone() for t in s["a"]], b=[t.clone() for t in s["b"]],
                          bias=None if s["bias"] is None else [t.clone() for t in s["bias"]], y=s["y"].clone())
-            d["buf"] = torch.zeros((len(sp.slices), n, sp.rank), dtype=torch.float32, device="cuda")
+            if sp.expand_only:
+                d["buf"] = d["x"]   # the layer's input is the expand input
+            else:
+                d["buf"] = torch.zeros((len(sp.slices), n, sp.rank), dtype=torch.float32, device="cuda")
             d["scale"] = sp.scale
+            d["expand_only"] = sp.expand_only
             self.layers.append(d)
 
     def prepare(self):
@@ -103,16 +107,18 @@ class DeviceSet:
     def step(self):
         self.prepare()
         for li in range(len(self.layers)):
-            self.shrink(li)
+            if not self.layers[li]["expand_only"]:
+                self.shrink(li)
             self.expand(li)
 
 
 def set_bytes(wl) -> int:
     tot = wl.mapping.numel() * 4
     for L in wl.layers:
-        tot += L.x.numel() * 2 + L.y0.numel() * 2
+        tot += L.x.numel() * L.x.element_size() + L.y0.numel() * 2
         tot += sum(t.numel() for t in L.lora_a) * 2 + sum(t.numel() for t in L.lora_b) * 2
-        tot += 4 * len(L.spec.slices) * wl.mapping.numel() * L.spec.rank
+        if not L.spec.expand_only:
+            tot += 4 * len(L.spec.slices) * wl.mapping.numel() * L.spec.rank
     return tot
 
 
@@ -156,10 +162,13 @@ def cpu_baseline(wl, budget_s: float) -> dict:
         oracle.prepare(m, wl.spec.max_loras)
         for L in wl.layers:
             sp = L.spec
-            xb = workloads.bf16_bits(L.x)[tokens]
-            buf = np.zeros((len(sp.slices), tokens.size, sp.rank), np.float32)
-            oracle.shrink(xb, [workloads.bf16_bits(a) for a in L.lora_a], buf, m[tokens], sp.scale,
-                          wl.spec.max_loras, nthreads=cores)
+            if sp.expand_only:
+                buf = np.ascontiguousarray(L.x.numpy()[:, tokens])
+            else:
+                xb = workloads.bf16_bits(L.x)[tokens]
+                buf = np.zeros((len(sp.slices), tokens.size, sp.rank), np.float32)
+                oracle.shrink(xb, [workloads.bf16_bits(a) for a in L.lora_a], buf, m[tokens], sp.scale,
+                              wl.spec.max_loras, nthreads=cores)
             y = np.ascontiguousarray(workloads.bf16_bits(L.y0)[tokens])
             bias = None if L.bias is None else [workloads.bf16_bits(b) for b in L.bias]
             oracle.expand(buf, [workloads.bf16_bits(b) for b in L.lora_b], bias, y, m[tokens],
@@ -334,12 +343,14 @@ def main():
 
     kern = {"prepare": per_launch(lambda s: s.prepare())}
     for li in range(nl):
-        kern["shrink%d" % li] = per_launch(lambda s: s.shrink(li))
+        if not wl.layers[li].spec.expand_only:
+            kern["shrink%d" % li] = per_launch(lambda s: s.shrink(li))
         kern["expand%d" % li] = per_launch(lambda s: s.expand(li))
     torch.cuda.synchronize()
     bytes_of = {"prepare": ab["prepare"]}
     for li in range(nl):
-        bytes_of["shrink%d" % li] = ab["shrink"][li]
+        if not wl.layers[li].spec.expand_only:
+            bytes_of["shrink%d" % li] = ab["shrink"][li]
         bytes_of["expand%d" % li] = ab["expand"][li]
     dom = max((k for k in kern if k != "prepare"), key=lambda k: kern[k])
     achieved = bytes_of[dom] / (kern[dom] * 1e-3) / 1e9
@@ -357,7 +368,9 @@ def main():
 
     spec = wl.spec
     layers_cfg = [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
-                   "scale": L.spec.scale, "bias": L.bias is not None} for L in wl.layers]
+                   "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
+                  for L in wl.layers]
+    step_desc = "prepare + " + " + ".join("expand" if L.spec.expand_only else "shrink + expand" for L in wl.layers)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -374,7 +387,7 @@ def main():
         "config": {"workload": spec.name, "num_tokens": n, "max_loras": spec.max_loras, "layers": layers_cfg,
                    "active_tokens": ab["T_a"], "active_loras": ab["L_a"], "parallelism": "none",
                    "launch": "eager" if args.eager else "hip_graph", "input_sets_rotated": rotate,
-                   "step": "prepare + %s" % " + ".join(["shrink + expand"] * nl)},
+                   "step": step_desc},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": bytes_of[dom], "avg_us": round(kern[dom] * 1e3, 3)},

@@ -5,9 +5,60 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "lora_internal.h"
 
 using namespace lora;
+
+// Workgroups of `fn` (256 threads, `lds` bytes of dynamic LDS) that the
+// device can hold at once: the register/wave limit per CU from the runtime's
+// occupancy query (cached per kernel and device), the LDS limit from the
+// kernel's static LDS plus `lds`, times the CU count.  Persistent grids are
+// capped at this so that no workgroup waits for another to exit.
+int lora::resident_grid(const void *fn, int threads, size_t lds) {
+    struct Entry {
+        const void *fn;
+        int dev, per_cu, cus;
+        size_t static_lds, lds_per_cu;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1 << 30;
+    Entry e{};
+    bool found = false;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (const Entry &c : cache)
+            if (c.fn == fn && c.dev == dev) {
+                e = c;
+                found = true;
+                break;
+            }
+    }
+    if (!found) {
+        e.fn = fn;
+        e.dev = dev;
+        hipFuncAttributes attr;
+        int v = 0;
+        e.per_cu = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, threads, 0) == hipSuccess && v > 0) ? v : 1;
+        e.cus = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 1;
+        e.lds_per_cu = (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && v > 0)
+                           ? (size_t)v : (size_t)65536;
+        e.static_lds = hipFuncGetAttributes(&attr, fn) == hipSuccess ? attr.sharedSizeBytes : 0;
+        std::lock_guard<std::mutex> g(mu);
+        cache.push_back(e);
+    }
+    const size_t per_block = e.static_lds + lds;
+    int per_cu = e.per_cu;
+    if (per_block > 0) {
+        const size_t by_lds = e.lds_per_cu / per_block;
+        if ((size_t)per_cu > by_lds) per_cu = (int)(by_lds > 0 ? by_lds : 1);
+    }
+    return per_cu * e.cus;
+}
 
 namespace {
 

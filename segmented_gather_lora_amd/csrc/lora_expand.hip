@@ -258,9 +258,6 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     a.tile_tokens = 16 * tt;
     const long tiles_upper = (n + a.tile_tokens - 1) / a.tile_tokens + segs;
     const long units_upper = tiles_upper * a.col_blocks;
-    const int cap = cfg.grid_cap > 0 ? cfg.grid_cap : 2048;
-    long grid = units_upper < cap ? units_upper : cap;
-    grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
     a.num_units = (int)units_upper;
     ExpandFn fn;
     const bool add = a.add_inputs != 0;
@@ -272,6 +269,8 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     }
     a.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
+    const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : 2048,
+                                      reinterpret_cast<const void *>(fn), kThreads, lds);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -301,6 +301,18 @@ struct ExpandTuning {
     int grid_cap;
 };
 
+// Workgroups of kernel `fn` the device holds at once (host side, cached).
+int resident_grid(const void *fn, int threads, size_t lds);
+// Persistent grid: at most `units` workgroups and at most what is resident at
+// once, a multiple of the XCD count (at least one workgroup per XCD).
+inline long persistent_grid(long units, long cap, const void *fn, int threads, size_t lds) {
+    long g = units < cap ? units : cap;
+    const long res = resident_grid(fn, threads, lds);
+    if (g > res) g = res;
+    g = g / kNumXcd * kNumXcd;
+    return g < kNumXcd ? kNumXcd : g;
+}
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream_t s);

@@ -545,14 +545,13 @@ hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStrea
     a.k_splits = ks;
     a.k_chunk = chunk;
     const long units_upper = (long)tiles_upper * a.row_blocks * ks;
-    const int cap = cfg.grid_cap > 0 ? cfg.grid_cap : (staged ? 512 : 1024);
-    long grid = units_upper < cap ? units_upper : cap;
-    grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
     a.num_units = (int)units_upper;
 
     // small batches: the direct-load kernel keeps the sorted indices in LDS
     a.meta.lds_tokens = (!staged && n <= kLdsTokensMax) ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
+    const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : (staged ? 512 : 1024),
+                                      reinterpret_cast<const void *>(fn), kThreads, lds);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

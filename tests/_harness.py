@@ -109,13 +109,18 @@ def oracle_layer(L: workloads.Layer, mapping: np.ndarray, max_loras: int, tokens
     sp = L.spec
     S, r = len(sp.slices), sp.rank
     msub = mapping[tokens]
-    xb = workloads.bf16_bits(L.x)[tokens]
-    buf = np.zeros((S, tokens.size, r), np.float32)
-    if buf_in is not None:
-        buf = np.ascontiguousarray(buf_in[:, tokens])
-    st, bound = oracle.shrink(xb, [workloads.bf16_bits(a) for a in L.lora_a], buf, msub, sp.scale,
-                              max_loras, with_bound=True, nthreads=nthreads)
-    assert st == 0
+    if sp.expand_only:
+        # the layer's input is the expand input itself
+        buf = np.ascontiguousarray(L.x.numpy()[:, tokens])
+        bound = np.zeros(buf.shape, np.float64)
+    else:
+        xb = workloads.bf16_bits(L.x)[tokens]
+        buf = np.zeros((S, tokens.size, r), np.float32)
+        if buf_in is not None:
+            buf = np.ascontiguousarray(buf_in[:, tokens])
+        st, bound = oracle.shrink(xb, [workloads.bf16_bits(a) for a in L.lora_a], buf, msub, sp.scale,
+                                  max_loras, with_bound=True, nthreads=nthreads)
+        assert st == 0
     if y_in is None:
         y = np.ascontiguousarray(workloads.bf16_bits(L.y0)[tokens])
     else:
@@ -193,8 +198,11 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         sp = L.spec
         D = DevLayer(L)
         S, r, O = len(sp.slices), sp.rank, sum(sp.slices)
-        buf = torch.zeros((S, n, r), dtype=torch.float32, device="cuda")
-        sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
+        if sp.expand_only:
+            buf = D.x.clone()
+        else:
+            buf = torch.zeros((S, n, r), dtype=torch.float32, device="cuda")
+            sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
         ldy = offset_start + O + ldy_extra
         y0full = torch.zeros((n, ldy), dtype=torch.bfloat16)
         y0full[:, offset_start:offset_start + O] = L.y0
@@ -210,7 +218,10 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         y_g = bits(y)
         y0b = bits(y0full)
         # untouched: -1 rows everywhere, columns outside the slices everywhere
-        assert np.all(buf_g[:, neg, :] == 0), "shrink touched a -1 row"
+        if sp.expand_only:
+            assert np.array_equal(buf_g, L.x.numpy()), "expand modified its input"
+        else:
+            assert np.all(buf_g[:, neg, :] == 0), "shrink touched a -1 row"
         assert np.array_equal(y_g[neg], y0b[neg]), "expand touched a -1 row"
         assert np.array_equal(y_g[:, :offset_start], y0b[:, :offset_start])
         assert np.array_equal(y_g[:, offset_start + O:], y0b[:, offset_start + O:])

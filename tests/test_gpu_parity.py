@@ -321,3 +321,95 @@ def test_shrink_staged_full_rows(monkeypatch):
     monkeypatch.setenv("LORA_SHRINK_VARIANT", "3")
     wl = workloads.random_case(230, 1000, 1024, (128, 64, 64), 64, 2, neg_fraction=0.0)
     H.run_and_check(wl, add_inputs=True)
+
+
+# ------------------------------------------------------------------ logits and embedding paths
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+def test_logits_path_full_size(add_inputs):
+    """The logits path at its full shape: shrink + expand over the per-prompt
+    mapping into one vocab-wide slice (128256 columns); every prompt checked."""
+    wl = workloads.make_workload("logits")
+    print("logits full size", add_inputs, flush=True)
+    print(H.run_and_check(wl, add_inputs=add_inputs), flush=True)
+
+
+def test_logits_path_ragged_vocab():
+    """A vocab width that is no multiple of the column block, with an offset."""
+    wl = workloads.random_case(301, 37, 512, (32008,), 16, 5, neg_fraction=0.2)
+    print("logits ragged vocab", flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=16)
+
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+@pytest.mark.parametrize("n,sample", [(333, None), (None, 1024)])
+def test_embedding_path(n, sample, add_inputs):
+    """The embedding path: expand only, one slice, from the fp32 [1][N][r] input."""
+    wl = workloads.make_workload("embedding", num_tokens=n)
+    print("embedding", n, sample, add_inputs, flush=True)
+    print(H.run_and_check(wl, add_inputs=add_inputs, sample=sample, seed=5), flush=True)
+
+
+# ------------------------------------------------------------------ graph-captured decode step
+
+def test_graph_captured_decode_step():
+    """prepare + shrink + expand captured once in a HIP graph on fixed buffers
+    (metadata allocated at maximum size, the batch's ids copied into a fixed
+    mapping buffer), then replayed for several batches, one of them all -1.
+    Eager work and synchronizations run between the replays, and every replay
+    is checked against the oracle on every token."""
+    sgl = H.lib()
+    base = workloads.make_workload("decode")
+    L = base.layers[0]
+    sp = L.spec
+    n, ml = base.mapping.numel(), base.spec.max_loras
+    S, r, O = len(sp.slices), sp.rank, sum(sp.slices)
+    meta = sgl.LoraMeta(ml, n)
+    host_flag = torch.full((1,), -7, dtype=torch.int32, pin_memory=True)
+    meta.struct.host_no_lora = host_flag.data_ptr()
+    D = H.DevLayer(L)
+    mapping_dev = torch.empty(n, dtype=torch.int32, device="cuda")
+    buf = torch.zeros((S, n, r), dtype=torch.float32, device="cuda")
+    y = torch.empty((n, O), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        sgl.lora_prepare_meta(mapping_dev, meta)
+        sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
+        sgl.lora_expand(buf, D.b, D.bias, y, meta, add_inputs=True)
+
+    mapping_dev.copy_(base.mapping)
+    y.copy_(D.y0)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(21)
+    y0b = workloads.bf16_bits(L.y0)
+    tokens = np.arange(n, dtype=np.int32)
+    for rep in range(5):
+        m = rng.integers(-1, ml, n).astype(np.int32)
+        if rep == 2:
+            m[:] = -1
+        mapping_dev.copy_(torch.from_numpy(m))
+        buf.zero_()
+        y.copy_(D.y0)
+        torch.cuda.synchronize()
+        print("graph replay", rep, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        H.check_meta(meta, m, ml)
+        assert int(host_flag[0]) == (1 if rep == 2 else 0)
+        buf_g = buf.cpu().numpy()
+        y_g = H.bits(y)
+        buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
+        H.shrink_check(buf_g, buf_ref, bound)
+        H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
+        neg = m == -1
+        assert np.all(buf_g[:, neg] == 0) and np.array_equal(y_g[neg], y0b[neg])
+    meta.struct.host_no_lora = None

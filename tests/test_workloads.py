@@ -43,3 +43,15 @@ def test_shapes_small_override():
     assert L.y0.shape == (40, 6144) and L.bias is None
     wl = workloads.make_workload("prefill", num_tokens=64)
     assert [b.shape for b in wl.layers[0].bias] == [(8, 4096), (8, 1024), (8, 1024)]
+
+
+def test_logits_and_embedding_shapes():
+    wl = workloads.make_workload("logits", num_tokens=8)
+    L = wl.layers[0]
+    assert L.x.shape == (8, 4096) and [b.shape for b in L.lora_b] == [(32, 128256, 16)]
+    assert L.y0.shape == (8, 128256)
+    wl = workloads.make_workload("embedding", num_tokens=40)
+    L = wl.layers[0]
+    assert L.spec.expand_only and L.lora_a == []
+    assert L.x.shape == (1, 40, 16) and L.x.dtype == torch.float32
+    assert [b.shape for b in L.lora_b] == [(32, 4096, 16)] and L.y0.shape == (40, 4096)

@@ -24,13 +24,24 @@ bias slices, y0; normal values are drawn in float32 and rounded to bfloat16):
   ids iid uniform 0..127 (tokens interleaved), then round(0.20 N) positions
   set to -1, scale 0.125, weights ~N(0, 0.01).
 * ``large_nolora``  the ``large`` shapes with every id -1 (seed 5).
+* ``logits``   N=256 prompts (one sampled position each), H=4096 -> one
+  vocab-wide slice [128256], r=16, max_loras=32, ids iid uniform 0..31, then
+  round(0.10 N) positions set to -1, scale 1.0 (the logits path: shrink +
+  expand over the per-prompt mapping).
+* ``embedding`` N=8192, expand only: input [1][N][16] fp32 ~N(0,1) -> one
+  slice [4096], r=16, max_loras=32, ids iid uniform 0..31, then round(0.10 N)
+  positions set to -1 (the embedding path).
 
 x and y0 are ~N(0,1); weights ~N(0,0.02) unless stated; sigma is the
 standard deviation.  "p % set to -1" picks exactly round(p N) positions with
 a seeded permutation.
 
+An expand-only layer draws, in order, its fp32 input ``x`` [1][N][r], the
+B slices, the bias slices (if any) and y0; it has no A.
+
 Storage layouts (the library's and the oracle's common input contract):
-``x`` [N][H] row-major; ``A_i`` [max_loras][r][H]; ``B_i`` [max_loras][O_i][r];
+``x`` [N][H] row-major (expand-only layers: fp32 [1][N][r]);
+``A_i`` [max_loras][r][H]; ``B_i`` [max_loras][O_i][r];
 ``bias_i`` [max_loras][O_i]; ``y0`` [N][sum O_i]; shrink buffer [S][N][r] fp32.
 """
 from __future__ import annotations
@@ -49,6 +60,7 @@ class LayerSpec:
     scale: float
     sigma_w: float = 0.02
     sigma_bias: Optional[float] = None
+    expand_only: bool = False    # no shrink: x is the fp32 expand input [1][N][r]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -90,6 +102,14 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
         "large_nolora", 5, 16384, 128, "all_neg",
         (LayerSpec(8192, (8192, 1024, 1024), 128, 0.125, sigma_w=0.01),),
         description="large shapes, every id -1"),
+    "logits": WorkloadSpec(
+        "logits", 6, 256, 32, "uniform", (LayerSpec(4096, (128256,), 16, 1.0),),
+        neg_fraction=0.10,
+        description="logits path: 256 prompts, H=4096 -> vocab 128256, r=16, max_loras=32, 10% -1"),
+    "embedding": WorkloadSpec(
+        "embedding", 7, 8192, 32, "uniform", (LayerSpec(16, (4096,), 16, 1.0, expand_only=True),),
+        neg_fraction=0.10,
+        description="embedding path: expand only, N=8192, input [N][16] fp32 -> 4096, max_loras=32, 10% -1"),
 }
 
 
@@ -135,8 +155,8 @@ def make_mapping(spec: WorkloadSpec, gen: torch.Generator) -> torch.Tensor:
 @dataclasses.dataclass
 class Layer:
     spec: LayerSpec
-    x: torch.Tensor                 # bf16 [N][H]
-    lora_a: List[torch.Tensor]      # bf16 [max_loras][r][H] per slice
+    x: torch.Tensor                 # bf16 [N][H]; expand-only layers: fp32 [1][N][r]
+    lora_a: List[torch.Tensor]      # bf16 [max_loras][r][H] per slice (none if expand-only)
     lora_b: List[torch.Tensor]      # bf16 [max_loras][O_i][r] per slice
     bias: Optional[List[torch.Tensor]]  # bf16 [max_loras][O_i] per slice, or None
     y0: torch.Tensor                # bf16 [N][sum O_i]
@@ -150,8 +170,12 @@ class Workload:
 
 
 def make_layer(spec: LayerSpec, n: int, max_loras: int, gen: torch.Generator) -> Layer:
-    x = _normal_bf16(gen, (n, spec.hidden), 1.0)
-    a = [_normal_bf16(gen, (max_loras, spec.rank, spec.hidden), spec.sigma_w) for _ in spec.slices]
+    if spec.expand_only:
+        x = torch.randn((1, n, spec.rank), generator=gen, dtype=torch.float32)
+        a = []
+    else:
+        x = _normal_bf16(gen, (n, spec.hidden), 1.0)
+        a = [_normal_bf16(gen, (max_loras, spec.rank, spec.hidden), spec.sigma_w) for _ in spec.slices]
     b = [_normal_bf16(gen, (max_loras, w, spec.rank), spec.sigma_w) for w in spec.slices]
     bias = None
     if spec.sigma_bias is not None:
