@@ -251,6 +251,7 @@ int lora_expand(const float *buf, int num_tokens, int rank, const void *const *l
     cfg.tile_tokens = env_int("LORA_EXPAND_TILE_TOKENS");
     if (cfg.tile_tokens % 16) cfg.tile_tokens = 0;
     cfg.grid_cap = env_int("LORA_EXPAND_GRID");
+    cfg.run_blocks = env_int("LORA_EXPAND_RUN");
     if (launch_expand(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }

@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return
 // Last valid 4-column group for a group starting at c (c % 4 == 0).
 __device__ __forceinline__ int clamp_group(int c, int width) { return c < width ? c : width - 4; }
 
-template <int KS, int TT, bool ADD>
+template <int KS, int TT, bool ADD, bool EARLY>
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     constexpr int kUnitTokens = 16 * TT;
     constexpr int kRowK = 32 * KS;              // bf16 per staged row (rank padded to 32)
@@ -71,20 +71,20 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     const int rank = a.rank;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 
-    const UnitWalker walk(total * a.col_blocks);
+    const UnitWalker walk(total * a.runs);
     for (int jj = walk.first;; jj += walk.stride) {
         const int u = walk.unit(jj);
         if (u < 0) break;
-        const int cb = u % a.col_blocks;
-        const TileRef tr = lookup_tile(smem, nslots, u / a.col_blocks);
+        const int run = u % a.runs;
+        const TileRef tr = lookup_tile(smem, nslots, u / a.runs);
         int i = 0;
 #pragma unroll
         for (int s = 1; s < LORA_MAX_SLICES; ++s)
-            if (s < a.num_slices && cb >= a.block_begin[s]) i = s;
+            if (s < a.num_slices && run >= a.run_begin[s]) i = s;
         const int width = select_slice(a.width, i);
-        const int c0 = (cb - select_slice(a.block_begin, i)) * kBlockCols + wave * kWaveCols;
-        const bool has_cols = c0 < width;   // wave-uniform; every wave still joins the barriers
-        const int cw = has_cols ? c0 : 0;
+        const int blocks_i = (width + kBlockCols - 1) / kBlockCols;
+        const int cb0 = (run - select_slice(a.run_begin, i)) * a.run_blocks;
+        const int ncb = min(a.run_blocks, blocks_i - cb0);
         const int pbase = tr.tile * kUnitTokens;
         const float *bufs = a.buf + (int64_t)i * a.num_tokens * rank;
 
@@ -108,42 +108,61 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
             t = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
             bvals[ps] = *reinterpret_cast<const floatx4 *>(bufs + (int64_t)t * rank + 4 * piece);
         }
-
-        // ---- this wave's weights: B operand of n-tile q, lane (n16, g) -> column 4*n16 + q
-        const int grp = clamp_group(cw + 4 * n16, width);    // first of this lane's 4 columns
-        const uint16_t *wbase = select_slice(a.b, i) + (int64_t)tr.lora_id * width * rank;
-        u32x4 w[4][KS];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint16_t *row = wbase + (int64_t)(grp + q) * rank;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int k = ks * 32 + 8 * g;
-                w[q][ks] = *reinterpret_cast<const u32x4 *>(row + (k < rank ? k : 0));
-            }
-        }
-        const uint16_t *bptr = select_slice(a.bias, i);
-        u32x2 braw = {0u, 0u};
-        if (bptr) braw = *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp);
-
-        // ---- y rows: tile q, row 4g + e of the tile -> token index
-        const int ycol = select_slice(a.col_off, i) + grp;
+        // ---- y rows of this lane: tile q, row 4g + e of the tile -> token index
         int ytok[TT][4];
-        u32x2 yv[TT][4];
 #pragma unroll
         for (int q = 0; q < TT; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 int pp = pbase + q * 16 + 4 * g + e;
                 pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
-                int t = sorted_at(a.meta, smem, tr.seg_start + pp);
-                t = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
-                ytok[q][e] = t;
-                if (ADD) yv[q][e] = *reinterpret_cast<const u32x2 *>(a.y + (int64_t)t * a.ldy + ycol);
-                else yv[q][e] = u32x2{0u, 0u};
+                const int t = sorted_at(a.meta, smem, tr.seg_start + pp);
+                ytok[q][e] = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
             }
 
-        // ---- stage the buffer rows in LDS as bf16 hi / lo (rank tail stays zero)
+        // ---- operands of one column block for this wave: weights (B operand of
+        // n-tile q: lane (n16, g) -> column 4*n16 + q), bias and y rows.  With
+        // EARLY (runs of one block) they are loaded before the buffer rows are
+        // staged, in the same round trip; longer runs load them block by block
+        // (fewer registers live across the staging).
+        const uint16_t *wslice = select_slice(a.b, i) + (int64_t)tr.lora_id * width * rank;
+        const uint16_t *bptr = select_slice(a.bias, i);
+        const int slice_col = select_slice(a.col_off, i);
+        u32x4 w[4][KS];
+        u32x2 braw, yv[TT][4];
+        // address of y[row][col], recomputed at every use: the opaque copy of
+        // the row keeps the compiler from holding 16 64-bit row addresses
+        // live across the column-block loop
+        auto y_at = [&](int row, int col) {
+            asm volatile("" : "+v"(row));
+            return a.y + ((int64_t)row * a.ldy + col);
+        };
+        auto load_block = [&](int grp) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t *row = wslice + (int64_t)(grp + q) * rank;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int k = ks * 32 + 8 * g;
+                    w[q][ks] = *reinterpret_cast<const u32x4 *>(row + (k < rank ? k : 0));
+                }
+            }
+            braw = bptr ? *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp) : u32x2{0u, 0u};
+            const int ycol = slice_col + grp;
+#pragma unroll
+            for (int q = 0; q < TT; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    yv[q][e] = ADD ? *reinterpret_cast<const u32x2 *>(y_at(ytok[q][e], ycol)) : u32x2{0u, 0u};
+        };
+        // first of this lane's 4 columns in block cb0 + c (clamped to the slice)
+        auto group_of = [&](int c) {
+            return clamp_group((cb0 + c) * kBlockCols + wave * kWaveCols + 4 * n16, width);
+        };
+        if (EARLY) load_block(group_of(0));
+
+        // ---- stage the buffer rows in LDS as bf16 hi / lo (rank tail stays zero),
+        // once for all column blocks of the run
 #pragma unroll
         for (int ps = 0; ps < kPasses; ++ps) {
             const int p = brow_p[ps];
@@ -166,21 +185,28 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
                 s_lo[p * kRowStride + k] = 0;
             }
         }
-        // K positions >= rank: zero the weights too (no NaN from stale data)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool kin = ks * 32 + 8 * g < rank;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w[q][ks] = kin ? w[q][ks] : z4;
-        }
-        float bias[4];
-        bias[0] = bf16_bits_to_float(braw[0] & 0xffffu);
-        bias[1] = bf16_bits_to_float(braw[0] >> 16);
-        bias[2] = bf16_bits_to_float(braw[1] & 0xffffu);
-        bias[3] = bf16_bits_to_float(braw[1] >> 16);
         __syncthreads();
 
-        if (has_cols) {
+        for (int c = 0; c < ncb; ++c) {
+            // a wave past the slice's last column stays past it for the rest of the run
+            if ((cb0 + c) * kBlockCols + wave * kWaveCols >= width) break;
+            const int grp = group_of(c);
+            if (!EARLY || c > 0) load_block(grp);
+
+            // K positions >= rank: zero the weights (no NaN from stale data)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bool kin = ks * 32 + 8 * g < rank;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q][ks] = kin ? w[q][ks] : z4;
+            }
+            float bias[4];
+            bias[0] = bf16_bits_to_float(braw[0] & 0xffffu);
+            bias[1] = bf16_bits_to_float(braw[0] >> 16);
+            bias[2] = bf16_bits_to_float(braw[1] & 0xffffu);
+            bias[3] = bf16_bits_to_float(braw[1] >> 16);
+            const int ycol = slice_col + grp;
+
 #pragma unroll
             for (int q = 0; q < TT; ++q) {
                 floatx4 acc[4];
@@ -205,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
                     const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][e] + bias[1]);
                     const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][e] + bias[2]);
                     const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][e] + bias[3]);
-                    *reinterpret_cast<u32x2 *>(a.y + (int64_t)ytok[q][e] * a.ldy + ycol) =
+                    *reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)) =
                         u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
                               pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
                 }
@@ -218,33 +244,41 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
 typedef void (*ExpandFn)(ExpandArgs);
 
 template <int KS, int TT>
-ExpandFn pick_add(bool add) {
-    return add ? expand_kernel<KS, TT, true> : expand_kernel<KS, TT, false>;
+ExpandFn pick_add(bool add, bool early) {
+    if (early) return add ? expand_kernel<KS, TT, true, true> : expand_kernel<KS, TT, false, true>;
+    return add ? expand_kernel<KS, TT, true, false> : expand_kernel<KS, TT, false, false>;
 }
 
 template <int KS>
-ExpandFn pick_tt(int tt, bool add) {
+ExpandFn pick_tt(int tt, bool add, bool early) {
     switch (tt) {
-        case 1: return pick_add<KS, 1>(add);
-        case 2: return pick_add<KS, 2>(add);
-        default: return pick_add<KS, 4>(add);
+        case 1: return pick_add<KS, 1>(add, early);
+        case 2: return pick_add<KS, 2>(add, early);
+        default: return pick_add<KS, 4>(add, early);
+    }
+}
+
+ExpandFn pick(int ks, int tt, bool add, bool early) {
+    switch (ks) {
+        case 1: return pick_tt<1>(tt, add, early);
+        case 2: return pick_tt<2>(tt, add, early);
+        case 3: return pick_tt<3>(tt, add, early);
+        default: return pick_tt<4>(tt, add, early);
     }
 }
 
 }  // namespace
 
-// Launch geometry from host-known sizes only: 256 columns per workgroup and
-// TT tiles of 16 tokens per unit, following the expected segment length
-// N / min(N, max_loras + 1).
+// Launch geometry from host-known sizes only: 256 columns per column block,
+// TT tiles of 16 tokens per unit following the expected segment length
+// N / min(N, max_loras + 1), and runs of R column blocks of one slice per unit
+// (the unit's buffer rows are staged once for its R blocks).  R is 1, with the
+// block's loads issued in the staging round trip, when units of one block fill
+// the resident grid at most twice or when a 64-token tile's buffer rows are
+// small (rank <= 16); otherwise R = 4 (measured best or within a few percent
+// on the prefill, Zipf, large and logits shapes).
 hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStream_t s) {
     ExpandArgs a = in;
-    int blocks = 0;
-    for (int i = 0; i < a.num_slices; ++i) {
-        a.block_begin[i] = blocks;
-        blocks += (a.width[i] + kBlockCols - 1) / kBlockCols;
-    }
-    for (int i = a.num_slices; i <= LORA_MAX_SLICES; ++i) a.block_begin[i] = blocks;
-    a.col_blocks = blocks;
     const int n = a.num_tokens;
     const int nslots = a.meta.nslots;
     const int segs = nslots < n ? nslots : n;
@@ -256,19 +290,34 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     }
     tt = tt >= 4 ? 4 : (tt >= 2 ? 2 : 1);
     a.tile_tokens = 16 * tt;
-    const long tiles_upper = (n + a.tile_tokens - 1) / a.tile_tokens + segs;
-    const long units_upper = tiles_upper * a.col_blocks;
-    a.num_units = (int)units_upper;
-    ExpandFn fn;
     const bool add = a.add_inputs != 0;
-    switch (ks) {
-        case 1: fn = pick_tt<1>(tt, add); break;
-        case 2: fn = pick_tt<2>(tt, add); break;
-        case 3: fn = pick_tt<3>(tt, add); break;
-        default: fn = pick_tt<4>(tt, add); break;
-    }
     a.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
+    const long tiles_upper = (n + a.tile_tokens - 1) / a.tile_tokens + segs;
+
+    auto count_runs = [&](int r) {
+        long runs = 0;
+        for (int i = 0; i < a.num_slices; ++i) {
+            a.run_begin[i] = (int)runs;
+            runs += ((a.width[i] + kBlockCols - 1) / kBlockCols + r - 1) / r;
+        }
+        for (int i = a.num_slices; i <= LORA_MAX_SLICES; ++i) a.run_begin[i] = (int)runs;
+        return runs;
+    };
+    int r = 1;
+    if (cfg.run_blocks > 0) {
+        r = cfg.run_blocks;
+    } else {
+        const long resident = resident_grid(reinterpret_cast<const void *>(pick(ks, tt, add, false)), kThreads, lds);
+        const bool few_units = tiles_upper * count_runs(1) <= 2 * resident;
+        const bool light_rows = tt == 4 && a.rank <= 16;   // little buffer to stage per unit
+        r = (few_units || light_rows) ? 1 : 4;
+    }
+    a.run_blocks = r;
+    a.runs = (int)count_runs(r);
+    const ExpandFn fn = pick(ks, tt, add, r == 1);
+    const long units_upper = tiles_upper * a.runs;
+    a.num_units = (int)units_upper;
     const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : 2048,
                                       reinterpret_cast<const void *>(fn), kThreads, lds);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);

@@ -275,11 +275,12 @@ struct ExpandArgs {
     int64_t ldy;
     int32_t width[LORA_MAX_SLICES];
     int32_t col_off[LORA_MAX_SLICES];      // first y column of each slice
-    int32_t block_begin[LORA_MAX_SLICES + 1];  // prefix of column blocks per slice
+    int32_t run_begin[LORA_MAX_SLICES + 1];    // prefix of column-block runs per slice
     int32_t num_slices;
     int32_t num_tokens;
     int32_t rank;
-    int32_t col_blocks;   // total column blocks
+    int32_t run_blocks;   // column blocks per run (the last run of a slice may be shorter)
+    int32_t runs;         // total runs
     int32_t tile_tokens;  // tokens per work unit (multiple of 16)
     int32_t num_units;
     int32_t add_inputs;
@@ -299,6 +300,7 @@ struct ShrinkTuning {
 struct ExpandTuning {
     int tile_tokens;       // 16, 32 or 64
     int grid_cap;
+    int run_blocks;        // column blocks per unit
 };
 
 // Workgroups of kernel `fn` the device holds at once (host side, cached).

@@ -205,6 +205,20 @@ def test_expand_tile_variants(tt, monkeypatch):
     H.run_and_check(wl, add_inputs=True)
 
 
+@pytest.mark.parametrize("run", [1, 2, 3, 8])
+@pytest.mark.parametrize("tt,rank", [(16, 16), (64, 64), (64, 128)])
+@pytest.mark.parametrize("add_inputs", [True, False])
+def test_expand_run_variants(run, tt, rank, add_inputs, monkeypatch):
+    """Units of one tile x a run of column blocks: slice widths whose block
+    counts the run does not divide, partial last blocks, bias, an offset."""
+    monkeypatch.setenv("LORA_EXPAND_RUN", str(run))
+    monkeypatch.setenv("LORA_EXPAND_TILE_TOKENS", str(tt))
+    wl = workloads.random_case(150 + run + tt + rank, 300, 64, (1800, 264, 8, 776), rank, 6, bias=True,
+                               neg_fraction=0.15)
+    print("expand run", run, tt, rank, add_inputs, flush=True)
+    H.run_and_check(wl, add_inputs=add_inputs, offset_start=16, ldy_extra=8)
+
+
 def _gpu_outputs(wl, meta, buf0=None):
     sgl = H.lib()
     L = wl.layers[0]
