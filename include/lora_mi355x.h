@@ -45,7 +45,8 @@ typedef enum lora_status {
     LORA_ERR_ALIGN = -6,         /* a bf16 / fp32 operand is not 16-byte aligned as required */
     LORA_ERR_SLICES = -7,        /* num_slices outside [1, LORA_MAX_SLICES] */
     LORA_ERR_LAUNCH = -8,        /* the HIP runtime rejected a kernel launch or copy */
-    LORA_ERR_ID_RANGE = -9       /* device-side only: written to meta->status by prepare */
+    LORA_ERR_ID_RANGE = -9,      /* device-side only: written to meta->status by prepare */
+    LORA_ERR_SYNC = -10          /* device-side only: a lora_shrink_expand wait timed out (meta->status) */
 } lora_status_t;
 
 #define LORA_MAX_LORAS 1023      /* ids 0 .. 1022; -1 = no LoRA */
@@ -66,6 +67,9 @@ typedef enum lora_status {
  *   no_lora_flag           int32[1]   1 when every id is -1 (or N == 0)
  *   status                 int32[1]   0, or LORA_ERR_ID_RANGE when some id was
  *                                     outside [-1, max_loras) (such ids count as -1)
+ *   sync                   int32[128 * (ceil(min(max_num_tokens, 24576) / 16)
+ *                                + min(max_loras + 1, max_num_tokens) + 1)]
+ *                                     counters of lora_shrink_expand
  * The struct itself lives in host memory; lora_prepare_meta() records
  * num_tokens in it.
  */
@@ -77,6 +81,9 @@ typedef struct lora_meta {
     int32_t *lora_token_start_loc;
     int32_t *no_lora_flag;
     int32_t *status;
+    int32_t *sync;           /* work counters of lora_shrink_expand (library-owned part of
+                                the region): zeroed by lora_prepare_meta, left zero by
+                                every lora_shrink_expand */
     int32_t *host_no_lora;   /* optional host pinned word (NULL = none): prepare copies
                                 no_lora_flag into it asynchronously on its stream */
     int32_t max_loras;
@@ -159,6 +166,33 @@ int lora_expand(const float *buf, int num_tokens, int rank,
                 const int *slice_widths, int num_slices,
                 void *y, int64_t ldy, int offset_start, int add_inputs,
                 const lora_meta_t *meta, hipStream_t stream);
+
+/*
+ * lora_shrink followed by lora_expand on the same buffer, as
+ * PunicaWrapperGPU.add_lora_linear on the "punica_gpu" page chains them
+ * (add_shrink into the fp32 buffer, then add_expand of that buffer), in one
+ * call: the arguments, layouts and results are exactly those of
+ *     lora_shrink(x, ldx, N, hidden, lora_a, S, rank, buf, meta, scale, stream);
+ *     lora_expand(buf, N, rank, lora_b, bias, slice_widths, S, y, ldy,
+ *                 offset_start, add_inputs, meta, stream);
+ * buf ends holding the shrink result (buf += scale * x A^T) and y the expand
+ * result.  For batches of short segments (decode-like: expected tokens per
+ * LoRA below 24, S * rank <= 64, rank <= 64) both steps run in one launch:
+ * the workgroups of each 16-token tile run its shrink parts, then wait on the
+ * device until every part is done before their share of the tile's expand
+ * (a waiter that sees no progress runs the parts nobody has started, so the
+ * wait needs no co-residency).  Other shapes launch the two kernels.  The fused
+ * launch uses meta->sync; calls sharing one metadata region must not overlap
+ * (they are ordered on one stream in normal use), and meta must have been
+ * prepared at least once since it was bound.  Errors are those of the two
+ * calls; a device-side wait that never ends (not expected) gives up after
+ * about 0.1 s and sets meta->status to LORA_ERR_SYNC.
+ */
+int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
+                       const void *const *lora_a, const void *const *lora_b, const void *const *bias,
+                       const int *slice_widths, int num_slices, int rank, float *buf,
+                       void *y, int64_t ldy, int offset_start, int add_inputs,
+                       const lora_meta_t *meta, float scale, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *lora_status_string(int status);

@@ -5,7 +5,7 @@ Torch tensors supply device memory and the current HIP stream.  The names
 mirror the C ABI in include/lora_mi355x.h:
 
     lora_meta_bytes, lora_meta_bind, lora_prepare_meta, lora_shrink,
-    lora_expand, lora_status_string
+    lora_expand, lora_shrink_expand, lora_status_string
 
 plus ``LoraMeta``, a holder that owns one device region sized by
 ``lora_meta_bytes`` (LoRAKernelMeta.make on the "lora_kernel_metadata" page)
@@ -33,13 +33,14 @@ LORA_ERR_ALIGN = -6
 LORA_ERR_SLICES = -7
 LORA_ERR_LAUNCH = -8
 LORA_ERR_ID_RANGE = -9
+LORA_ERR_SYNC = -10
 
 LORA_MAX_LORAS = 1023
 LORA_MAX_SLICES = 8
 LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
-            "lora_expand", "lora_status_string")
+            "lora_expand", "lora_shrink_expand", "lora_status_string")
 
 
 class LoraError(RuntimeError):
@@ -57,6 +58,7 @@ class lora_meta_t(ctypes.Structure):
         ("lora_token_start_loc", ctypes.c_void_p),
         ("no_lora_flag", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("sync", ctypes.c_void_p),
         ("host_no_lora", ctypes.c_void_p),
         ("max_loras", ctypes.c_int32),
         ("max_num_tokens", ctypes.c_int32),
@@ -82,6 +84,9 @@ def _load() -> ctypes.CDLL:
     lib.lora_expand.restype = i32
     lib.lora_expand.argtypes = [P, i32, i32, P, P, P, i32, P, i64, i32, i32,
                                 ctypes.POINTER(lora_meta_t), P]
+    lib.lora_shrink_expand.restype = i32
+    lib.lora_shrink_expand.argtypes = [P, i64, i32, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
+                                       ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [i32]
     return lib
@@ -152,7 +157,8 @@ class LoraMeta:
                     num_tokens_per_lora=self._view("num_tokens_per_lora", L + 1),
                     lora_token_start_loc=self._view("lora_token_start_loc", L + 2),
                     no_lora_flag=self._view("no_lora_flag", 1),
-                    status=self._view("status", 1))
+                    status=self._view("status", 1),
+                    sync=self._view("sync", 1))
 
 
 def lora_prepare_meta(mapping, meta: LoraMeta, stream=None) -> None:
@@ -185,3 +191,18 @@ def lora_expand(buf, lora_b: Sequence, bias: Optional[Sequence], y, meta: LoraMe
     _check(lib.lora_expand(buf.data_ptr(), n, r, bptrs, biasptrs, widths, s, y.data_ptr(), y.stride(0),
                            int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
                            _stream(stream)), "lora_expand")
+
+
+def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], buf, y,
+                       meta: LoraMeta, scale: float, offset_start: int = 0, add_inputs: bool = True,
+                       stream=None) -> None:
+    """lora_shrink then lora_expand on the same buffer, in one call (one
+    launch for decode-like batches).  Arguments as for the two calls."""
+    n, h = x.shape
+    s, _, r = buf.shape
+    widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
+    biasptrs = None if bias is None else _ptr_array(bias)
+    _check(lib.lora_shrink_expand(x.data_ptr(), x.stride(0), n, h, _ptr_array(lora_a), _ptr_array(lora_b),
+                                  biasptrs, widths, s, r, buf.data_ptr(), y.data_ptr(), y.stride(0),
+                                  int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
+                                  float(scale), _stream(stream)), "lora_shrink_expand")

@@ -88,7 +88,7 @@ MetaView view_of(const lora_meta_t *m) {
 int check_meta(const lora_meta_t *m) {
     if (!m) return LORA_ERR_NULL;
     if (!m->token_lora_mapping || !m->token_indices_sorted || !m->active_lora_ids ||
-        !m->num_tokens_per_lora || !m->lora_token_start_loc || !m->no_lora_flag || !m->status)
+        !m->num_tokens_per_lora || !m->lora_token_start_loc || !m->no_lora_flag || !m->status || !m->sync)
         return LORA_ERR_NULL;
     if (m->max_loras < 1 || m->max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
     if (m->max_num_tokens < 0 || m->max_num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
@@ -104,7 +104,8 @@ size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
         return 0;
     const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
     return 2 * tok + 2 * round_up(sizeof(int32_t) * (max_loras + 1)) +
-           round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign;
+           round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign +
+           round_up(sizeof(int32_t) * (size_t)fused_sync_words(max_num_tokens, max_loras + 1));
 }
 
 int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out) {
@@ -130,6 +131,8 @@ int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, l
     out->no_lora_flag = reinterpret_cast<int32_t *>(p);
     p += kAlign;
     out->status = reinterpret_cast<int32_t *>(p);
+    p += kAlign;
+    out->sync = reinterpret_cast<int32_t *>(p);
     out->host_no_lora = nullptr;
     out->max_loras = max_loras;
     out->max_num_tokens = max_num_tokens;
@@ -152,6 +155,8 @@ int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta,
     a.start_loc = meta->lora_token_start_loc;
     a.no_lora = meta->no_lora_flag;
     a.status = meta->status;
+    a.sync = meta->sync;
+    a.sync_tiles = num_tokens <= kFusedMaxTokens ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
     a.num_tokens = num_tokens;
     a.max_loras = meta->max_loras;
     if (launch_prepare(a, stream) != hipSuccess) return LORA_ERR_LAUNCH;
@@ -164,9 +169,15 @@ int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta,
     return LORA_OK;
 }
 
-int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const void *const *lora_a,
-                int num_slices, int rank, float *buf, const lora_meta_t *meta, float scale,
-                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and kernel arguments of lora_shrink; `skip` is set when there is no
+// work (num_tokens == 0).
+int shrink_args(const void *x, int64_t ldx, int num_tokens, int hidden, const void *const *lora_a,
+                int num_slices, int rank, float *buf, const lora_meta_t *meta, float scale, ShrinkArgs &a,
+                bool &skip) {
     int st = check_meta(meta);
     if (st) return st;
     if (meta->num_tokens < 0 || num_tokens != meta->num_tokens) return LORA_ERR_NUM_TOKENS;
@@ -179,10 +190,10 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
         if (!lora_a[i]) return LORA_ERR_NULL;
         if (!aligned16(lora_a[i])) return LORA_ERR_ALIGN;
     }
-    if (num_tokens == 0) return LORA_OK;
+    skip = num_tokens == 0;
+    if (skip) return LORA_OK;
     if (!aligned16(x) || !aligned16(buf)) return LORA_ERR_ALIGN;
 
-    ShrinkArgs a;
     memset(&a, 0, sizeof a);
     a.meta = view_of(meta);
     a.x = static_cast<const uint16_t *>(x);
@@ -194,6 +205,10 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     a.rank = rank;
     a.rows = num_slices * rank;
     a.scale = scale;
+    return LORA_OK;
+}
+
+ShrinkTuning shrink_tuning() {
     ShrinkTuning cfg;
     cfg.tile_tokens = env_int("LORA_SHRINK_TILE_TOKENS");
     cfg.waves_k = env_int("LORA_SHRINK_WAVES_K");
@@ -202,13 +217,13 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     cfg.grid_cap = env_int("LORA_SHRINK_GRID");
     cfg.variant = env_int("LORA_SHRINK_VARIANT");
     cfg.staged_cfg = env_int("LORA_SHRINK_STAGED");
-    if (launch_shrink(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
-    return LORA_OK;
+    return cfg;
 }
 
-int lora_expand(const float *buf, int num_tokens, int rank, const void *const *lora_b, const void *const *bias,
+// Checks and kernel arguments of lora_expand.
+int expand_args(const float *buf, int num_tokens, int rank, const void *const *lora_b, const void *const *bias,
                 const int *slice_widths, int num_slices, void *y, int64_t ldy, int offset_start, int add_inputs,
-                const lora_meta_t *meta, hipStream_t stream) {
+                const lora_meta_t *meta, ExpandArgs &a, bool &skip) {
     int st = check_meta(meta);
     if (st) return st;
     if (meta->num_tokens < 0 || num_tokens != meta->num_tokens) return LORA_ERR_NUM_TOKENS;
@@ -226,10 +241,10 @@ int lora_expand(const float *buf, int num_tokens, int rank, const void *const *l
     }
     if (total > ldy) return LORA_ERR_SHAPE;
     if (num_tokens > 0 && (!buf || !y)) return LORA_ERR_NULL;
-    if (num_tokens == 0) return LORA_OK;
+    skip = num_tokens == 0;
+    if (skip) return LORA_OK;
     if (!aligned16(buf) || !aligned16(y)) return LORA_ERR_ALIGN;
 
-    ExpandArgs a;
     memset(&a, 0, sizeof a);
     a.meta = view_of(meta);
     a.buf = buf;
@@ -247,12 +262,69 @@ int lora_expand(const float *buf, int num_tokens, int rank, const void *const *l
     a.num_tokens = num_tokens;
     a.rank = rank;
     a.add_inputs = add_inputs ? 1 : 0;
+    return LORA_OK;
+}
+
+ExpandTuning expand_tuning() {
     ExpandTuning cfg;
     cfg.tile_tokens = env_int("LORA_EXPAND_TILE_TOKENS");
     if (cfg.tile_tokens % 16) cfg.tile_tokens = 0;
     cfg.grid_cap = env_int("LORA_EXPAND_GRID");
     cfg.run_blocks = env_int("LORA_EXPAND_RUN");
-    if (launch_expand(a, cfg, stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    return cfg;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const void *const *lora_a,
+                int num_slices, int rank, float *buf, const lora_meta_t *meta, float scale,
+                hipStream_t stream) {
+    ShrinkArgs a;
+    bool skip = false;
+    const int st = shrink_args(x, ldx, num_tokens, hidden, lora_a, num_slices, rank, buf, meta, scale, a, skip);
+    if (st || skip) return st;
+    if (launch_shrink(a, shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    return LORA_OK;
+}
+
+int lora_expand(const float *buf, int num_tokens, int rank, const void *const *lora_b, const void *const *bias,
+                const int *slice_widths, int num_slices, void *y, int64_t ldy, int offset_start, int add_inputs,
+                const lora_meta_t *meta, hipStream_t stream) {
+    ExpandArgs a;
+    bool skip = false;
+    const int st = expand_args(buf, num_tokens, rank, lora_b, bias, slice_widths, num_slices, y, ldy, offset_start,
+                               add_inputs, meta, a, skip);
+    if (st || skip) return st;
+    if (launch_expand(a, expand_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    return LORA_OK;
+}
+
+int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, const void *const *lora_a,
+                       const void *const *lora_b, const void *const *bias, const int *slice_widths,
+                       int num_slices, int rank, float *buf, void *y, int64_t ldy, int offset_start,
+                       int add_inputs, const lora_meta_t *meta, float scale, hipStream_t stream) {
+    ShrinkArgs sa;
+    ExpandArgs ea;
+    bool skip = false;
+    int st = shrink_args(x, ldx, num_tokens, hidden, lora_a, num_slices, rank, buf, meta, scale, sa, skip);
+    if (st) return st;
+    st = expand_args(buf, num_tokens, rank, lora_b, bias, slice_widths, num_slices, y, ldy, offset_start,
+                     add_inputs, meta, ea, skip);
+    if (st || skip) return st;
+    const bool fused_allowed = env_int("LORA_FUSED") >= 0;   // LORA_FUSED=-1: always two launches
+    if (fused_allowed) {
+        // test knobs: polls before a waiter helps (default 128), owners leaving
+        // their parts to the waiters (forces the helping path)
+        const int help = getenv("LORA_FUSED_HELP_AFTER") ? env_int("LORA_FUSED_HELP_AFTER") : 128;
+        const hipError_t e = launch_fused(sa, ea, meta->sync, meta->status, help, env_int("LORA_FUSED_OWNERS_SKIP"),
+                                          stream);
+        if (e == hipSuccess) return LORA_OK;
+        if (e != hipErrorNotSupported) return LORA_ERR_LAUNCH;
+    }
+    if (launch_shrink(sa, shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    if (launch_expand(ea, expand_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }
 
@@ -268,6 +340,7 @@ const char *lora_status_string(int status) {
         case LORA_ERR_SLICES: return "num_slices out of range";
         case LORA_ERR_LAUNCH: return "HIP launch failed";
         case LORA_ERR_ID_RANGE: return "a LoRA id was outside [-1, max_loras) and was treated as -1";
+        case LORA_ERR_SYNC: return "a fused shrink-expand wait on the device timed out";
         default: return "unknown status";
     }
 }

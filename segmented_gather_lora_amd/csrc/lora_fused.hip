@@ -1,0 +1,510 @@
+// lora_fused.hip -- lora_shrink followed by lora_expand in one launch, for
+// batches of short segments (PunicaWrapperGPU.add_lora_linear on the
+// "punica_gpu" page chains add_shrink into an fp32 buffer and add_expand of
+// that buffer; decode batches give each LoRA a handful of tokens, where two
+// launches and two metadata round trips cost more than the data).
+//
+// Work is cut into 16-token tiles of the segments, as in the two kernels.
+// Each tile gets W workgroups (grid / tiles, or one workgroup walks several
+// tiles when tiles outnumber the grid); workgroup idx of a tile
+//   1. runs the tile's shrink parts idx, idx + W, ... (a part is a K chunk of
+//      all S*r <= 64 weight rows; its partial sums are added into buf with
+//      float atomics), marking each part taken (an exchange on its flag,
+//      issued as the part starts and checked before its adds) and counting
+//      it done;
+//   2. takes the tile's 256-column expand blocks idx, idx + W, ..., issues
+//      the first block's weight and y loads, waits until the done counter
+//      shows every part, stages the tile's buffer rows of all slices in LDS
+//      once, and runs its blocks.
+// The wait cannot deadlock, whatever is resident: a waiter that sees no
+// progress for a while (about 0.1 ms) takes every part whose flag is still
+// clear and runs it itself, so it only ever waits for parts that a running
+// workgroup has taken, and a part never waits.  An owner that finds its part
+// taken skips the adds.  Expand blocks have no dependants.
+//
+// Ordering without cache maintenance: buf is only written here with
+// device-scope atomic adds, which are performed at the device's coherence
+// point; a part's writer waits until its adds have completed (vmcnt) before
+// it counts the part; readers load buf with device-coherent loads after they
+// see the count.  (A device-scope release / acquire fence would instead write
+// back / invalidate the XCD's whole L2 at every part and every reader.)
+//
+// Counters (in the caller's metadata region, zeroed by prepare), per tile T
+// in kFusedTileWords words of their own:
+//   +kFusedPastWait   workgroups done with parts and waits;
+//   +kFusedPartsDone  parts done (its own 128-byte line: it is polled);
+//   +kFusedFlags + p  part p taken.
+// The W-th workgroup done with parts and waits resets the tile's words, so a
+// call leaves every counter at zero.
+#include "lora_internal.h"
+
+#include <string.h>
+
+namespace lora {
+
+struct FusedArgs {
+    ShrinkArgs s;
+    ExpandArgs e;
+    int32_t *sync;
+    int32_t *status;
+    int32_t blocks;         // expand column blocks per tile (all slices)
+    int32_t block_begin[LORA_MAX_SLICES + 1];   // prefix of column blocks per slice
+    int32_t help_after;     // polls without progress before a waiter takes free parts
+    int32_t owners_skip;    // test only: owners leave their parts to the waiters
+};
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTile = 16;            // tokens per tile
+constexpr int kBlockCols = 256;      // expand columns per unit
+constexpr int kWaveCols = 64;
+constexpr int kSpinLimit = 1 << 18;  // polls about 0.5 us apart: ~0.1 s
+// s_waitcnt vmcnt(0) with the other counters left at their maximum
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+__device__ __forceinline__ int clamp_group(int c, int width) { return c < width ? c : width - 4; }
+
+template <typename T, int N>
+__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
+    T r = p[0];
+#pragma unroll
+    for (int s = 1; s < N; ++s)
+        if (i == s) r = p[s];
+    return r;
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+__device__ __forceinline__ void reset_tile(int32_t *words, int parts) {
+    __hip_atomic_store(words + kFusedPartsDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(words + kFusedPastWait, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int p = 0; p < parts; ++p) __hip_atomic_store(words + kFusedFlags + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// MT: 16-row tiles of weight rows (S*r <= 16*MT); KS: 32-wide K steps of the
+// expand (rank <= 32*KS).
+template <int MT, int KS, bool ADD>
+__global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
+    constexpr int kRowK = 32 * KS;
+    constexpr int kRowStride = kRowK + 8;
+    constexpr int kMaxSlices = (16 * MT) / 8;   // S * r <= 16*MT with r >= 8
+    extern __shared__ int smem[];
+    __shared__ int s_wsum[kWaves];
+    __shared__ int s_claim;
+    __shared__ int s_tok[kTile];   // the tile's token indices, for the helper path
+    __shared__ floatx4 red[(kWaves - 1) * MT * kWave];
+    // buffer rows of the tile, every slice: [slice][token][k]
+    __shared__ __attribute__((aligned(16))) uint16_t s_hi[kMaxSlices * kTile * kRowStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_lo[kMaxSlices * kTile * kRowStride];
+
+    const ShrinkArgs &a = f.s;
+    const ExpandArgs &e = f.e;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int n16 = lane & 15, g = lane >> 4;
+    const int rank = a.rank;
+
+    const int nslots = a.meta.nslots;
+    const int total = build_tile_table<kThreads>(a.meta, kTile, smem, s_wsum);
+    if (total == 0) return;
+    const int grid = gridDim.x, b = blockIdx.x;
+    // this workgroup's tiles: one tile shared by W workgroups, or every grid-th tile alone
+    const bool shared = grid >= total;
+    const int first = shared ? b % total : b;
+    const int step = shared ? total : grid;
+    const int idx = shared ? b / total : 0;
+
+    for (int tile = first; tile < total; tile += step) {
+        const int W = shared ? grid / total + (tile < grid % total ? 1 : 0) : 1;
+        int32_t *const words = f.sync + kFusedTileWords * tile;
+        int32_t *const parts_done = words + kFusedPartsDone;
+        int32_t *const past_wait = words + kFusedPastWait;
+        int32_t *const flags = words + kFusedFlags;
+        const TileRef tr = lookup_tile(smem, nslots, tile);
+
+        // One shrink part on the MFMA: K chunk `ks` of all weight rows for the
+        // tile's tokens.  The owner takes the part's flag as it starts and
+        // skips the adds if a waiter took it first.
+        auto run_part = [&](int ks) {
+            int got = 0;
+            const int p = tr.tile * kTile + n16;
+            bool tv = p < tr.seg_count;
+            int tok = sorted_at(a.meta, smem, tr.seg_start + (tv ? p : tr.seg_count - 1));
+            if ((unsigned)tok >= (unsigned)a.num_tokens) {
+                tok = 0;
+                tv = false;
+            }
+            const uint16_t *xrow = a.x + (int64_t)tok * a.ldx;
+            const uint16_t *arow[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                int row = mt * 16 + n16;
+                row = row < a.rows ? row : a.rows - 1;
+                const int i = row / rank, j = row - i * rank;
+                arow[mt] = select_slice(a.a, i) + ((int64_t)tr.lora_id * rank + j) * a.hidden;
+            }
+            const int kbeg = ks * a.k_chunk;
+            const int kend = min(kbeg + a.k_chunk, a.hidden);
+            const int nsteps = (kend - kbeg + 63) / 64;
+            floatx4 acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            // K steps interleaved over the 4 waves, the next step in flight while
+            // one is multiplied; loads are unconditional (past the end: the row
+            // start, masked below)
+            auto load = [&](int st, u32x4 (&av)[MT][2], u32x4 (&xv)[2]) {
+                const int kk = kbeg + st * 64 + g * 16;
+                const int o0 = kk + 8 <= kend ? kk : 0, o1 = kk + 16 <= kend ? kk + 8 : 0;
+                xv[0] = ld16(xrow + o0);
+                xv[1] = ld16(xrow + o1);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    av[mt][0] = ld16(arow[mt] + o0);
+                    av[mt][1] = ld16(arow[mt] + o1);
+                }
+            };
+            u32x4 av[MT][2], xv[2];
+            load(min(wave, nsteps - 1), av, xv);
+            // the flag exchange after the first loads: memory counters complete
+            // in order, so the first step does not wait for its round trip
+            if (tid == 0) got = __hip_atomic_exchange(&flags[ks], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int st = wave; st < nsteps; st += kWaves) {
+                u32x4 an[MT][2], xn[2];
+                load(min(st + kWaves, nsteps - 1), an, xn);
+                const int kk = kbeg + st * 64 + g * 16;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (kk + 8 * h + 8 > kend) {
+                        xv[h] = z;
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) av[mt][h] = z;
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = mfma16x16x32(as_bf16x8(av[mt][h]), as_bf16x8(xv[h]), acc[mt]);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    xv[h] = xn[h];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) av[mt][h] = an[mt][h];
+                }
+            }
+            if (wave > 0) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) red[((wave - 1) * MT + mt) * kWave + lane] = acc[mt];
+            }
+            __syncthreads();
+            // wave 0 holds thread 0's exchange result in lane 0
+            if (wave == 0 && __builtin_amdgcn_readfirstlane(got) == 0) {
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] += red[((w - 1) * MT + mt) * kWave + lane];
+                // D layout: lane holds rows 4g..4g+3 of m-tile mt for token column n16
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row0 = mt * 16 + 4 * g;
+                    if (!tv || row0 >= a.rows) continue;
+                    const int i = row0 / rank, j = row0 - i * rank;
+                    float *dst = a.buf + ((int64_t)i * a.num_tokens + tok) * rank + j;
+                    const floatx4 v = acc[mt] * a.scale;
+                    unsafeAtomicAdd(dst + 0, v[0]);
+                    unsafeAtomicAdd(dst + 1, v[1]);
+                    unsafeAtomicAdd(dst + 2, v[2]);
+                    unsafeAtomicAdd(dst + 3, v[3]);
+                }
+                // this wave's additions have completed before the part is counted
+                __builtin_amdgcn_s_waitcnt(kVmcntZero);
+                asm volatile("" ::: "memory");
+                if (lane == 0) __hip_atomic_fetch_add(parts_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();   // `red` is reused
+        };
+
+        // The same part for a waiter that took its flag (a rare path, kept
+        // small so that it costs the main path no registers): one fp32 dot
+        // product per (token, weight row) over the K chunk.
+        auto help_part = [&](int ks) {
+            const int kbeg = ks * a.k_chunk;
+            const int kend = min(kbeg + a.k_chunk, a.hidden);   // kend - kbeg is a multiple of 8
+            if (tid < kTile) {   // -1: no token at this tile row
+                const int pp = tr.tile * kTile + tid;
+                const int t = sorted_at(a.meta, smem, tr.seg_start + (pp < tr.seg_count ? pp : tr.seg_count - 1));
+                s_tok[tid] = (pp < tr.seg_count && (unsigned)t < (unsigned)a.num_tokens) ? t : -1;
+            }
+            __syncthreads();
+            for (int o = tid; o < kTile * a.rows; o += kThreads) {
+                const int pr = o / a.rows, row = o - pr * a.rows;
+                const int tok = s_tok[pr];
+                if (tok < 0) continue;
+                const int i = row / rank, j = row - i * rank;
+                const uint16_t *xr = a.x + (int64_t)tok * a.ldx;
+                const uint16_t *ar = select_slice(a.a, i) + ((int64_t)tr.lora_id * rank + j) * a.hidden;
+                float sum = 0.f;
+                for (int k = kbeg; k < kend; k += 8) {
+                    const u32x4 xv = ld16(xr + k), av = ld16(ar + k);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        sum += bf16_bits_to_float(xv[c] & 0xffffu) * bf16_bits_to_float(av[c] & 0xffffu);
+                        sum += bf16_bits_to_float(xv[c] >> 16) * bf16_bits_to_float(av[c] >> 16);
+                    }
+                }
+                unsafeAtomicAdd(a.buf + ((int64_t)i * a.num_tokens + tok) * rank + j, sum * a.scale);
+            }
+            // every thread's additions have completed before the part is counted
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            asm volatile("" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(parts_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+
+        // ---------------- 1. this workgroup's own shrink parts
+        if (!f.owners_skip)
+            for (int ks = idx; ks < a.k_splits; ks += W) run_part(ks);
+
+        // ---------------- 2. expand blocks idx, idx + W, ... of the tile
+        bool waited = false;
+        for (int blk = idx; blk < f.blocks; blk += W) {
+            int i = 0;
+#pragma unroll
+            for (int s = 1; s < LORA_MAX_SLICES; ++s)
+                if (s < e.num_slices && blk >= f.block_begin[s]) i = s;
+            const int width = select_slice(e.width, i);
+            const int c0 = (blk - select_slice(f.block_begin, i)) * kBlockCols + wave * kWaveCols;
+            const bool has_cols = c0 < width;
+            const int grp = clamp_group((has_cols ? c0 : 0) + 4 * n16, width);
+
+            // weights, bias and y rows first: they do not depend on buf
+            const uint16_t *wslice = select_slice(e.b, i) + (int64_t)tr.lora_id * width * rank;
+            const uint16_t *bptr = select_slice(e.bias, i);
+            const int ycol = select_slice(e.col_off, i) + grp;
+            u32x4 w[4][KS];
+            u32x2 braw, yv[4];
+            int ytok[4];
+            auto load_block = [&]() {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const uint16_t *row = wslice + (int64_t)(grp + qq) * rank;
+#pragma unroll
+                    for (int k = 0; k < KS; ++k) {
+                        const int kk = k * 32 + 8 * g;
+                        w[qq][k] = ld16(row + (kk < rank ? kk : 0));
+                    }
+                }
+                braw = bptr ? *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp) : u32x2{0u, 0u};
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    int pp = tr.tile * kTile + 4 * g + r4;
+                    pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
+                    const int tt = sorted_at(e.meta, smem, tr.seg_start + pp);
+                    ytok[r4] = (unsigned)tt < (unsigned)e.num_tokens ? tt : e.num_tokens - 1;
+                    yv[r4] = ADD ? *reinterpret_cast<const u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + ycol)
+                                 : u32x2{0u, 0u};
+                }
+            };
+            load_block();
+
+            if (!waited) {   // uniform: the first block of this tile
+                waited = true;
+                // wait for every part; after help_after polls without them,
+                // take and run every part still free, then wait for the rest
+                for (int round = 0;; ++round) {
+                    if (tid == 0) {
+                        const int limit = round == 0 ? f.help_after : kSpinLimit;
+                        int n = 0;
+                        bool ok;
+                        while (!(ok = __hip_atomic_load(parts_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                                      a.k_splits) && n < limit) {
+                            ++n;
+                            __builtin_amdgcn_s_sleep(8);
+                        }
+                        s_claim = ok ? 1 : (round == 0 ? 2 : 3);
+                        if (s_claim == 3)
+                            __hip_atomic_store(f.status, (int)LORA_ERR_SYNC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    __syncthreads();
+                    const int verdict = s_claim;
+                    __syncthreads();
+                    if (verdict != 2) break;
+                    for (int ks = 0; ks < a.k_splits; ++ks) {
+                        if (tid == 0) s_claim = __hip_atomic_exchange(&flags[ks], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __syncthreads();
+                        const int taken = s_claim;
+                        __syncthreads();
+                        if (!taken) help_part(ks);
+                    }
+                }
+                // the tile's buffer rows of every slice (device-coherent loads), as bf16 hi / lo
+                const int lanes_per_row = rank >> 2;
+                const int per_slice = kTile * lanes_per_row;   // 16-byte pieces per slice
+                for (int x = tid; x < e.num_slices * per_slice; x += kThreads) {
+                    const int si = x / per_slice, rem = x % per_slice;
+                    const int prow = rem / lanes_per_row, piece = rem % lanes_per_row;
+                    int pp = tr.tile * kTile + prow;
+                    pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
+                    int tt = sorted_at(e.meta, smem, tr.seg_start + pp);
+                    tt = (unsigned)tt < (unsigned)e.num_tokens ? tt : e.num_tokens - 1;
+                    const float *src = e.buf + ((int64_t)si * e.num_tokens + tt) * rank + 4 * piece;
+                    floatx4 bv;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        bv[k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    uint32_t h[4], l[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        h[k] = float_to_bf16_bits(bv[k]);
+                        l[k] = float_to_bf16_bits(bv[k] - bf16_bits_to_float(h[k]));
+                    }
+                    const int o = (si * kTile + prow) * kRowStride + 4 * piece;
+                    *reinterpret_cast<u32x2 *>(&s_hi[o]) = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+                    *reinterpret_cast<u32x2 *>(&s_lo[o]) = u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+                }
+                if (rank < kRowK) {
+                    for (int x = tid; x < e.num_slices * kTile * (kRowK - rank); x += kThreads) {
+                        const int pr = x / (kRowK - rank), k = rank + x % (kRowK - rank);
+                        s_hi[pr * kRowStride + k] = 0;
+                        s_lo[pr * kRowStride + k] = 0;
+                    }
+                }
+                __syncthreads();
+                // done with parts and waits: the tile's last such workgroup
+                // resets its words (no exchange, count or poll of them is left)
+                if (tid == 0) {
+                    const int d = __hip_atomic_fetch_add(past_wait, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (d == W - 1) reset_tile(words, a.k_splits);
+                }
+            }
+
+            if (has_cols) {
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const bool kin = k * 32 + 8 * g < rank;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) w[qq][k] = kin ? w[qq][k] : z4;
+                }
+                floatx4 acc[4];
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) acc[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const int off = (i * kTile + n16) * kRowStride + k * 32 + 8 * g;
+                    const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_hi[off]);
+                    const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lo[off]);
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        acc[t4] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(w[t4][k]), acc[t4]);
+                        acc[t4] = mfma16x16x32(as_bf16x8(al), as_bf16x8(w[t4][k]), acc[t4]);
+                    }
+                }
+                float bias[4];
+                bias[0] = bf16_bits_to_float(braw[0] & 0xffffu);
+                bias[1] = bf16_bits_to_float(braw[0] >> 16);
+                bias[2] = bf16_bits_to_float(braw[1] & 0xffffu);
+                bias[3] = bf16_bits_to_float(braw[1] >> 16);
+                // acc[t4][r4]: token row 4g + r4 of the tile, column grp + t4
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const u32x2 yy = yv[r4];
+                    const float r0 = bf16_bits_to_float(yy[0] & 0xffffu) + (acc[0][r4] + bias[0]);
+                    const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][r4] + bias[1]);
+                    const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][r4] + bias[2]);
+                    const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][r4] + bias[3]);
+                    *reinterpret_cast<u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + ycol) =
+                        u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                              pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
+                }
+            }
+        }
+        if (!waited && tid == 0) {
+            // no expand block here: this workgroup is done with its parts, count it out
+            const int d = __hip_atomic_fetch_add(past_wait, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == W - 1) reset_tile(words, a.k_splits);
+        }
+        __syncthreads();   // the staged rows are rewritten for the next tile
+    }
+}
+
+typedef void (*FusedFn)(FusedArgs);
+
+template <int MT>
+FusedFn pick_ks(int ks, bool add) {
+    if (ks == 1) return add ? fused_kernel<MT, 1, true> : fused_kernel<MT, 1, false>;
+    return add ? fused_kernel<MT, 2, true> : fused_kernel<MT, 2, false>;
+}
+
+FusedFn pick(int mt, int ks, bool add) {
+    switch (mt) {
+        case 1: return pick_ks<1>(ks, add);
+        case 2: return pick_ks<2>(ks, add);
+        case 3: return pick_ks<3>(ks, add);
+        default: return pick_ks<4>(ks, add);
+    }
+}
+
+}  // namespace
+
+// Range: expected tokens per segment below 24, S * rank <= 64, rank <= 64.
+// K is split into chunks of 64-multiples until about 256 shrink parts exist,
+// as for the direct shrink kernel; the grid is what the device holds at once.
+hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *sync, int32_t *status,
+                        int help_after, int owners_skip, hipStream_t stream) {
+    const int n = sin.num_tokens;
+    const int nslots = sin.meta.nslots;
+    const int segs = nslots < n ? nslots : n;
+    const int avg = (n + segs - 1) / segs;
+    if (avg >= 24 || n > kFusedMaxTokens || sin.rows > 64 || sin.rank > 64) return hipErrorNotSupported;
+
+    FusedArgs f;
+    memset(&f, 0, sizeof f);
+    f.s = sin;
+    f.e = ein;
+    f.sync = sync;
+    f.status = status;
+    f.help_after = help_after;
+    f.owners_skip = owners_skip;
+    int blocks = 0;
+    for (int i = 0; i < ein.num_slices; ++i) {
+        f.block_begin[i] = blocks;
+        blocks += (ein.width[i] + kBlockCols - 1) / kBlockCols;
+    }
+    for (int i = ein.num_slices; i <= LORA_MAX_SLICES; ++i) f.block_begin[i] = blocks;
+    f.blocks = blocks;
+
+    const int max_ks = (sin.hidden + 255) / 256;
+    const long busy = (n + kTile - 1) / kTile + (segs + 1) / 2;
+    int ks = busy < 256 ? (int)((256 + busy - 1) / busy) : 1;
+    if (ks > max_ks) ks = max_ks;
+    if (ks > kFusedMaxParts) ks = kFusedMaxParts;
+    if (ks < 1) ks = 1;
+    int chunk = (sin.hidden + ks - 1) / ks;
+    chunk = (chunk + 63) / 64 * 64;
+    ks = (sin.hidden + chunk - 1) / chunk;
+    f.s.k_splits = ks;
+    f.s.k_chunk = chunk;
+    f.s.row_blocks = 1;
+    f.s.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
+    f.e.meta.lds_tokens = f.s.meta.lds_tokens;
+
+    const int mt = (sin.rows + 15) / 16;
+    const int kse = (sin.rank + 31) / 32;
+    const FusedFn fn = pick(mt, kse, ein.add_inputs != 0);
+    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + f.s.meta.lds_tokens);
+    // enough workgroups for every tile's parts and blocks, at most what is resident
+    const long tiles_upper = (n + kTile - 1) / kTile + segs;
+    long grid = resident_grid(reinterpret_cast<const void *>(fn), kThreads, lds);
+    const long useful = tiles_upper * (blocks > ks ? blocks : ks);
+    if (grid > useful) grid = useful;
+    grid = grid / kNumXcd * kNumXcd;
+    if (grid < kNumXcd) grid = kNumXcd;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, stream, f);
+    return hipGetLastError();
+}
+
+}  // namespace lora

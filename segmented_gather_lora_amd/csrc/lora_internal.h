@@ -245,6 +245,8 @@ struct PrepareArgs {
     int32_t *start_loc;
     int32_t *no_lora;
     int32_t *status;
+    int32_t *sync;        // work counters of the fused call, zeroed here
+    int32_t sync_tiles;   // tiles whose counters the batch can use (0: none)
     int32_t num_tokens;
     int32_t max_loras;
 };
@@ -319,5 +321,26 @@ inline long persistent_grid(long units, long cap, const void *fn, int threads, s
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream_t s);
 hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream_t s);
+// Fused shrink -> expand for short segments.  Returns hipErrorNotSupported
+// (launching nothing) when the shape is outside the fused kernel's range; the
+// caller then launches shrink and expand.
+hipError_t launch_fused(const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync, int32_t *status,
+                        int help_after, int owners_skip, hipStream_t stream);
+
+// The fused call serves batches of short segments only: fewer than 24
+// tokens per LoRA on average, so at most kFusedMaxTokens tokens.
+constexpr long kFusedMaxTokens = 24L * (LORA_MAX_LORAS + 1);
+// Words of the fused call's counter area for batches of up to n tokens and
+// nslots slots: 128 words (512 bytes) per 16-token tile: the exit counter,
+// the polled done counter on a 128-byte line of its own, and one taken flag
+// per shrink part (at most kFusedMaxParts).
+constexpr int kFusedTileWords = 128;
+constexpr int kFusedPastWait = 0, kFusedPartsDone = 32, kFusedFlags = 64;   // word offsets
+constexpr int kFusedMaxParts = 64;
+inline long fused_tiles(long n, long nslots) {
+    if (n > kFusedMaxTokens) n = kFusedMaxTokens;
+    return (n + 15) / 16 + (nslots < n ? nslots : n) + 1;
+}
+inline long fused_sync_words(long n, long nslots) { return kFusedTileWords * fused_tiles(n, nslots); }
 
 }  // namespace lora

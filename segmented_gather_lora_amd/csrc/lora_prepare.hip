@@ -60,6 +60,12 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
         s_any = 0;
         s_bad = 0;
     }
+    // the fused call's counters start every batch at zero (each fused call
+    // also leaves them zero)
+    for (int k = tid; k < a.sync_tiles * (2 + kFusedMaxParts); k += kThreads) {
+        const int tile = k / (2 + kFusedMaxParts), w = k % (2 + kFusedMaxParts);
+        a.sync[kFusedTileWords * tile + (w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + w - 2)] = 0;
+    }
     __syncthreads();
 
     // ---- 1. ranks within the wave's slice

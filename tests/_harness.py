@@ -181,9 +181,10 @@ def expand_check(y_gpu: np.ndarray, y_ref: np.ndarray, y0: np.ndarray, mag: np.n
 
 
 def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int | None = None,
-                  seed: int = 0, offset_start: int = 0, ldy_extra: int = 0) -> dict:
-    """prepare + (shrink, expand) per layer on the GPU; metadata, buffer and
-    output compared with the oracle (all tokens, or a seeded sample)."""
+                  seed: int = 0, offset_start: int = 0, ldy_extra: int = 0, fused: bool = False) -> dict:
+    """prepare + (shrink, expand) per layer on the GPU -- or the one
+    lora_shrink_expand call with `fused` -- with metadata, buffer and output
+    compared with the oracle (all tokens, or a seeded sample)."""
     sgl = lib()
     mapping = wl.mapping.numpy()
     n, ml = mapping.size, wl.spec.max_loras
@@ -202,7 +203,8 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
             buf = D.x.clone()
         else:
             buf = torch.zeros((S, n, r), dtype=torch.float32, device="cuda")
-            sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
+            if not fused:
+                sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
         ldy = offset_start + O + ldy_extra
         y0full = torch.zeros((n, ldy), dtype=torch.bfloat16)
         y0full[:, offset_start:offset_start + O] = L.y0
@@ -212,8 +214,14 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
             y0full[:, :offset_start] = fill[:, :offset_start]
             y0full[:, offset_start + O:] = fill[:, offset_start + O:]
         y = y0full.to("cuda")
-        sgl.lora_expand(buf, D.b, D.bias, y, meta, offset_start=offset_start, add_inputs=add_inputs)
+        if fused and not sp.expand_only:
+            sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale, offset_start=offset_start,
+                                   add_inputs=add_inputs)
+        else:
+            sgl.lora_expand(buf, D.b, D.bias, y, meta, offset_start=offset_start, add_inputs=add_inputs)
         torch.cuda.synchronize()
+        if fused:
+            check_sync_clear(meta, n)
         buf_g = buf.cpu().numpy()
         y_g = bits(y)
         y0b = bits(y0full)
@@ -236,6 +244,23 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         stats["expand_ratio"] = max(stats["expand_ratio"], ex["ratio"])
         stats["literal_rel"] = max(stats["literal_rel"], ex["literal_rel"])
     return stats
+
+
+def sync_words(n: int, max_loras: int) -> int:
+    """Counter words of the fused call for a batch of n tokens: 128 per
+    16-token tile (ceil(min(n, 24576)/16) + min(slots, n) + 1 tiles)."""
+    nn = min(n, 24576)
+    return 128 * ((nn + 15) // 16 + min(max_loras + 1, nn) + 1)
+
+
+def check_sync_clear(meta, n: int) -> None:
+    """Every fused call leaves its counters at zero and reports no timeout."""
+    v = meta.views()
+    off = meta.struct.sync - meta.region.data_ptr()
+    words = meta.region[off:off + 4 * sync_words(n, meta.max_loras)].view(torch.int32).cpu().numpy()
+    counters = words.reshape(-1, 128)[:, [0, 32] + list(range(64, 128))]
+    assert np.all(counters == 0), "fused counters not reset: %s" % counters[np.any(counters != 0, axis=1)][:4]
+    assert int(v["status"][0]) in (0, lib().LORA_ERR_ID_RANGE), "status %d" % int(v["status"][0])
 
 
 def run_expand_only(wl: workloads.Workload, add_inputs: bool, seed: int = 1) -> dict:

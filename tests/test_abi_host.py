@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(sgl):
 
 
 def test_status_strings(sgl):
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = sgl.lora_status_string(code)
         assert s and s != "unknown status"
     assert sgl.lora_status_string(-100) == "unknown status"
@@ -55,7 +55,8 @@ def test_meta_bytes_and_bind(sgl):
     base = 0x7f0000000000
     m = sgl.lora_meta_bind(base, nb, 3, 64)
     spans = [(m.token_lora_mapping, 4 * 64), (m.token_indices_sorted, 4 * 64), (m.active_lora_ids, 16),
-             (m.num_tokens_per_lora, 16), (m.lora_token_start_loc, 20), (m.no_lora_flag, 4), (m.status, 4)]
+             (m.num_tokens_per_lora, 16), (m.lora_token_start_loc, 20), (m.no_lora_flag, 4), (m.status, 4),
+             (m.sync, 4 * 128 * (64 // 16 + 4 + 1))]
     spans.sort()
     for (p, sz), (q, _) in zip(spans, spans[1:]):
         assert p + sz <= q
@@ -140,6 +141,33 @@ def test_expand_rejects(sgl):
     assert call(bias=_ptrs(None, 0x70008)) == sgl.LORA_ERR_ALIGN
     assert call(y=Y + 2) == sgl.LORA_ERR_ALIGN and call(buf=BUF + 8) == sgl.LORA_ERR_ALIGN
     assert call(y=None) == sgl.LORA_ERR_NULL
+    assert call(n=0, meta=_fake_meta(sgl, 0)) == sgl.LORA_OK
+
+
+def test_shrink_expand_rejects(sgl):
+    """The fused call checks both halves' arguments, before any launch."""
+    L = sgl.lib
+    A = _ptrs(0x10000, 0x20000)
+    B = _ptrs(0x30000, 0x40000)
+    W = (ctypes.c_int * 2)(64, 32)
+    X, BUF, Y = 0x50000, 0x60000, 0x70000
+    m = _fake_meta(sgl, 32)
+    ok = dict(x=X, ldx=64, n=32, h=64, a=A, b=B, bias=None, w=W, s=2, r=16, buf=BUF, y=Y, ldy=96, off=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.lora_shrink_expand(a["x"], a["ldx"], a["n"], a["h"], a["a"], a["b"], a["bias"], a["w"], a["s"],
+                                    a["r"], a["buf"], a["y"], a["ldy"], a["off"], 1,
+                                    ctypes.byref(kw.get("meta", m)), 1.0, None)
+    assert call(n=31) == sgl.LORA_ERR_NUM_TOKENS
+    assert call(s=0) == sgl.LORA_ERR_SLICES
+    assert call(h=60) == sgl.LORA_ERR_SHAPE and call(r=12) == sgl.LORA_ERR_SHAPE
+    assert call(w=(ctypes.c_int * 2)(64, 12)) == sgl.LORA_ERR_SHAPE and call(ldy=88) == sgl.LORA_ERR_SHAPE
+    assert call(a=_ptrs(0x10000, None)) == sgl.LORA_ERR_NULL and call(b=_ptrs(None, 0x40000)) == sgl.LORA_ERR_NULL
+    assert call(x=X + 8) == sgl.LORA_ERR_ALIGN and call(y=Y + 2) == sgl.LORA_ERR_ALIGN
+    mm = _fake_meta(sgl, 32)
+    mm.sync = None
+    assert call(meta=mm) == sgl.LORA_ERR_NULL
     assert call(n=0, meta=_fake_meta(sgl, 0)) == sgl.LORA_OK
 
 

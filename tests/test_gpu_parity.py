@@ -427,3 +427,126 @@ def test_graph_captured_decode_step():
         neg = m == -1
         assert np.all(buf_g[:, neg] == 0) and np.array_equal(y_g[neg], y0b[neg])
     meta.struct.host_no_lora = None
+
+
+# ------------------------------------------------------------------ fused shrink -> expand
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+@pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("decode", 37), ("logits", None),
+                                    ("zipf", 300), ("prefill", 600), ("large", 160)])
+def test_fused_parity(name, n, add_inputs):
+    """lora_shrink_expand against the oracle on every token: one launch for the
+    decode-like shapes (decode, tiny, logits, a short Zipf batch), the two
+    kernels for the others (prefill, rank 128)."""
+    wl = workloads.make_workload(name, num_tokens=n)
+    print("fused", name, n, add_inputs, flush=True)
+    print(H.run_and_check(wl, add_inputs=add_inputs, fused=True), flush=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=401, n=1, hidden=64, slices=(8,), rank=8, max_loras=1, neg_fraction=0.0),
+    dict(seed=402, n=45, hidden=200, slices=(24, 40), rank=8, max_loras=7, bias=True),
+    dict(seed=403, n=130, hidden=1032, slices=(264, 8, 520), rank=16, max_loras=9, bias=True),
+    dict(seed=404, n=200, hidden=72, slices=(1800,), rank=64, max_loras=40),
+    dict(seed=405, n=300, hidden=4104, slices=(512, 256), rank=32, max_loras=1023, neg_fraction=0.3),
+    dict(seed=406, n=2600, hidden=512, slices=(128, 128), rank=24, max_loras=200),
+    dict(seed=407, n=97, hidden=4096, slices=(8,) * 8, rank=8, max_loras=17, bias=True),
+])
+def test_fused_edge_shapes(case):
+    """Ragged K, ranks 8..64, widths off the 256-column block, 1023 LoRAs, a
+    batch past the sorted-index LDS copy, eight slices, bias and an offset."""
+    wl = workloads.random_case(**case)
+    print("fused edge", case["seed"], flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, fused=True)
+
+
+def test_fused_repeated_calls_and_no_lora():
+    """Several fused calls on one prepared batch (the counters must come back
+    to zero after each), then a no-LoRA batch, then a new batch."""
+    sgl = H.lib()
+    ml, n = 32, 256
+    meta = sgl.LoraMeta(ml, 512)
+    rng = np.random.default_rng(31)
+    for m in (rng.integers(-1, ml, n).astype(np.int32), np.full(n, -1, np.int32),
+              rng.integers(0, 3, 150).astype(np.int32)):
+        mt = torch.from_numpy(m)
+        sgl.lora_prepare_meta(mt.cuda(), meta)
+        for layer in range(3):
+            wl = workloads.random_case(500 + layer, m.size, 1024, (256, 64, 64), 16, ml, bias=layer == 1)
+            wl.mapping.copy_(mt)
+            L = wl.layers[0]
+            D = H.DevLayer(L)
+            buf = torch.zeros((3, m.size, 16), dtype=torch.float32, device="cuda")
+            y = D.y0.clone()
+            sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, L.spec.scale)
+            torch.cuda.synchronize()
+            H.check_sync_clear(meta, m.size)
+            tokens = np.arange(m.size, dtype=np.int32)
+            buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
+            buf_g, y_g = buf.cpu().numpy(), H.bits(y)
+            H.shrink_check(buf_g, buf_ref, bound)
+            H.expand_check(y_g, y_ref, workloads.bf16_bits(L.y0), mag, True, H.propagated(L, m, buf_ref, bound))
+
+
+def test_fused_graph_replay():
+    """prepare + lora_shrink_expand captured once and replayed for several
+    batches (one all -1), with eager work between replays."""
+    sgl = H.lib()
+    base = workloads.make_workload("decode")
+    L = base.layers[0]
+    sp = L.spec
+    n, ml = base.mapping.numel(), base.spec.max_loras
+    meta = sgl.LoraMeta(ml, n)
+    D = H.DevLayer(L)
+    mapping_dev = base.mapping.cuda()
+    buf = torch.zeros((3, n, sp.rank), dtype=torch.float32, device="cuda")
+    y = D.y0.clone()
+
+    def step():
+        sgl.lora_prepare_meta(mapping_dev, meta)
+        sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(41)
+    y0b = workloads.bf16_bits(L.y0)
+    tokens = np.arange(n, dtype=np.int32)
+    for rep in range(5):
+        m = rng.integers(-1, ml, n).astype(np.int32)
+        if rep == 3:
+            m[:] = -1
+        mapping_dev.copy_(torch.from_numpy(m))
+        buf.zero_()
+        y.copy_(D.y0)
+        torch.cuda.synchronize()
+        print("fused graph replay", rep, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        H.check_meta(meta, m, ml)
+        H.check_sync_clear(meta, n)
+        buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
+        buf_g, y_g = buf.cpu().numpy(), H.bits(y)
+        H.shrink_check(buf_g, buf_ref, bound)
+        H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
+
+
+@pytest.mark.parametrize("mode", ["owners_skip", "help_at_once"])
+@pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None)])
+def test_fused_helping_path(name, n, mode, monkeypatch):
+    """The waiters' fallback, forced from the host: with owners leaving their
+    parts, every part is run by waiters that take it by its flag; with no
+    patience at all, owners and waiters race for every part.  Results and the
+    counters' reset must be the same as on the normal path."""
+    monkeypatch.setenv("LORA_FUSED_HELP_AFTER", "0")
+    if mode == "owners_skip":
+        monkeypatch.setenv("LORA_FUSED_OWNERS_SKIP", "1")
+    wl = workloads.make_workload(name, num_tokens=n)
+    print("fused helping", name, mode, flush=True)
+    H.run_and_check(wl, add_inputs=True, fused=True)
