@@ -111,12 +111,24 @@ class DeviceSet:
         sgl.lora_shrink_expand(d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta, d["scale"],
                                offset_start=0, add_inputs=True)
 
-    def step(self, fused: bool = True):
-        self.prepare()
-        for li in range(len(self.layers)):
+    def prepare_linear(self, li):
+        """prepare + shrink + expand of one layer in one lora_prepare_shrink_expand call."""
+        import segmented_gather_lora_amd as sgl
+        d = self.layers[li]
+        sgl.lora_prepare_shrink_expand(self.mapping, d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta,
+                                       d["scale"], offset_start=0, add_inputs=True)
+
+    def step(self, path: str = "prepare_fused"):
+        first = 0
+        if path == "prepare_fused" and not self.layers[0]["expand_only"]:
+            self.prepare_linear(0)
+            first = 1
+        else:
+            self.prepare()
+        for li in range(first, len(self.layers)):
             if self.layers[li]["expand_only"]:
                 self.expand(li)
-            elif fused:
+            elif path in ("fused", "prepare_fused"):
                 self.linear(li)
             else:
                 self.shrink(li)
@@ -220,7 +232,8 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
                 continue
             name = r["Kernel_Name"]
             key = ("prepare" if "prepare_kernel" in name else "shrink" if "shrink_kernel" in name else
-                   "expand" if "expand_kernel" in name else "linear" if "fused_kernel" in name else
+                   "expand" if "expand_kernel" in name else
+                   ("preplinear" if "true>" in name.split(",")[-1] else "linear") if "fused_kernel" in name else
                    "copy" if ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()) else None)
             if key:
                 vals[key].append(float(r["Counter_Value"]) * 1024.0)
@@ -235,7 +248,7 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     wscale = copy_bytes / cw if cw else 1.0
     rec = {"workload": workload, "kernel_hash": kernel_source_hash(), "command": command,
            "copy_fetch_scale": fscale, "copy_write_scale": wscale, "traffic_bytes": {}, "raw": {}}
-    for k in ("prepare", "shrink", "expand", "linear"):
+    for k in ("prepare", "shrink", "expand", "linear", "preplinear"):
         if f.get(k) and w.get(k):
             fb = sum(f[k]) / len(f[k])
             wb = sum(w[k]) / len(w[k])
@@ -264,8 +277,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
-    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
-                    help="per layer: one lora_shrink_expand call, or lora_shrink then lora_expand")
+    ap.add_argument("--path", choices=("prepare_fused", "fused", "separate"), default="prepare_fused",
+                    help="prepare_fused: lora_prepare_shrink_expand for the first layer, lora_shrink_expand for "
+                         "the others; fused: lora_prepare_meta, then lora_shrink_expand per layer; separate: "
+                         "lora_prepare_meta, then lora_shrink and lora_expand per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate through (0 = auto)")
@@ -306,16 +321,16 @@ def main():
     nl = len(wl.layers)
 
     # warm-up (eager; loads the code objects), then capture one step per set
-    fused = args.path == "fused"
+    path = args.path
     for i in range(max(args.warmup, rotate)):
-        sets[i % rotate].step(fused)
+        sets[i % rotate].step(path)
     torch.cuda.synchronize()
 
     if args.profile_steps:
         # short eager run for hardware-counter collection, plus a plain copy
         # of known size that calibrates the byte counters
         for i in range(args.profile_steps):
-            sets[i % rotate].step(fused)
+            sets[i % rotate].step(path)
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -328,11 +343,11 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            sets[i % rotate].step(fused)
+            sets[i % rotate].step(path)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     else:
-        g = capture(lambda: [s.step(fused) for s in sets])
+        g = capture(lambda: [s.step(path) for s in sets])
         for _ in range(max(1, args.warmup // rotate)):
             g.replay()
         torch.cuda.synchronize()
@@ -361,6 +376,8 @@ def main():
             kern["shrink%d" % li] = per_launch(lambda s: s.shrink(li))
             kern["linear%d" % li] = per_launch(lambda s: s.linear(li))
         kern["expand%d" % li] = per_launch(lambda s: s.expand(li))
+    if not wl.layers[0].spec.expand_only:
+        kern["preplinear0"] = per_launch(lambda s: s.prepare_linear(0))
     torch.cuda.synchronize()
     bytes_of = {"prepare": ab["prepare"]}
     for li in range(nl):
@@ -368,18 +385,25 @@ def main():
             bytes_of["shrink%d" % li] = ab["shrink"][li]
             bytes_of["linear%d" % li] = ab["shrink"][li] + ab["expand"][li]
         bytes_of["expand%d" % li] = ab["expand"][li]
-    # the calls the timed step makes (besides prepare)
+    if "preplinear0" in kern:
+        bytes_of["preplinear0"] = ab["prepare"] + ab["shrink"][0] + ab["expand"][0]
+    # the calls the timed step makes
     used = []
     for li in range(nl):
         if wl.layers[li].spec.expand_only:
             used.append("expand%d" % li)
-        elif fused:
+        elif li == 0 and path == "prepare_fused":
+            used.append("preplinear0")
+        elif path in ("fused", "prepare_fused"):
             used.append("linear%d" % li)
         else:
             used += ["shrink%d" % li, "expand%d" % li]
-    dom = max(used, key=lambda k: kern[k])
+    if "preplinear0" not in used:
+        used.insert(0, "prepare")
+    dom = max((k for k in used if k != "prepare"), key=lambda k: kern[k])
     achieved = bytes_of[dom] / (kern[dom] * 1e-3) / 1e9
-    kname = {"shrink": "lora_shrink", "expand": "lora_expand", "linear": "lora_shrink_expand"}[dom[:6]]
+    kname = {"shrink": "lora_shrink", "expand": "lora_expand", "linear": "lora_shrink_expand",
+             "prepli": "lora_prepare_shrink_expand"}[dom[:6]]
     traffic = load_traffic(args.workload, dom)
     separate = [k for k in kern if k[:6] in ("shrink", "expand")]
     se_ms = sum(kern[k] for k in separate)
@@ -398,8 +422,15 @@ def main():
     layers_cfg = [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
                    "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
                   for L in wl.layers]
-    step_desc = "prepare + " + " + ".join(
-        "expand" if L.spec.expand_only else ("shrink_expand" if fused else "shrink + expand") for L in wl.layers)
+    parts = []
+    for li, L in enumerate(wl.layers):
+        if L.spec.expand_only:
+            parts.append("expand")
+        elif li == 0 and path == "prepare_fused":
+            parts.append("prepare_shrink_expand")
+        else:
+            parts.append("shrink_expand" if path != "separate" else "shrink + expand")
+    step_desc = ("" if "preplinear0" in used else "prepare + ") + " + ".join(parts)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -421,7 +452,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": bytes_of[dom], "avg_us": round(kern[dom] * 1e3, 3)},
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kern.items()},
-        "layer_calls": {"path": args.path, "us": round(calls_ms * 1e3, 3),
+        "step_calls": {"path": args.path, "us": round(calls_ms * 1e3, 3),
                         "tokens_per_s": round(n / (calls_ms * 1e-3), 1),
                         "GBps": round(calls_bytes / (calls_ms * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(calls_bytes / (calls_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},

@@ -194,6 +194,25 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
                        void *y, int64_t ldy, int offset_start, int add_inputs,
                        const lora_meta_t *meta, float scale, hipStream_t stream);
 
+/*
+ * lora_prepare_meta followed by lora_shrink_expand: a batch's metadata and its
+ * first LoRA layer (LoRAKernelMeta.prepare_tensors on the "lora_kernel_metadata"
+ * page, then PunicaWrapperGPU.add_lora_linear on the "punica_gpu" page), with
+ * the arguments and results of those two calls.  For batches of at most 2048
+ * tokens in the fused call's range it is one launch: every workgroup sorts
+ * the mapping in its own LDS (the same stable counting sort as
+ * lora_prepare_meta) and workgroup 0 writes the metadata arrays.  Otherwise
+ * the two calls are made.  As for lora_shrink_expand, meta must have been
+ * prepared at least once since it was bound (its counters start at zero).
+ * Records meta->num_tokens and copies the no-LoRA flag to meta->host_no_lora
+ * when that is set.
+ */
+int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const void *x, int64_t ldx, int hidden,
+                               const void *const *lora_a, const void *const *lora_b, const void *const *bias,
+                               const int *slice_widths, int num_slices, int rank, float *buf, void *y,
+                               int64_t ldy, int offset_start, int add_inputs, lora_meta_t *meta, float scale,
+                               hipStream_t stream);
+
 /* Static description of a status code. */
 const char *lora_status_string(int status);
 

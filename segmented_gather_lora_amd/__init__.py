@@ -5,15 +5,15 @@ Torch tensors supply device memory and the current HIP stream.  The names
 mirror the C ABI in include/lora_mi355x.h:
 
     lora_meta_bytes, lora_meta_bind, lora_prepare_meta, lora_shrink,
-    lora_expand, lora_shrink_expand, lora_status_string
+    lora_expand, lora_shrink_expand, lora_prepare_shrink_expand, lora_status_string
 
 plus ``LoraMeta``, a holder that owns one device region sized by
 ``lora_meta_bytes`` (LoRAKernelMeta.make on the "lora_kernel_metadata" page)
 and exposes its arrays as tensor views.
 
-Importing this package loads the library; it raises if the library has not
-been built (``python -m segmented_gather_lora_amd._build``): there is no
-fallback implementation.
+The library is loaded on the first call; that call raises ImportError if the
+library has not been built (``python -m segmented_gather_lora_amd._build``):
+there is no fallback implementation.
 """
 from __future__ import annotations
 
@@ -40,7 +40,7 @@ LORA_MAX_SLICES = 8
 LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
-            "lora_expand", "lora_shrink_expand", "lora_status_string")
+            "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_status_string")
 
 
 class LoraError(RuntimeError):
@@ -87,16 +87,34 @@ def _load() -> ctypes.CDLL:
     lib.lora_shrink_expand.restype = i32
     lib.lora_shrink_expand.argtypes = [P, i64, i32, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
                                        ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
+    lib.lora_prepare_shrink_expand.restype = i32
+    lib.lora_prepare_shrink_expand.argtypes = [P, i32, P, i64, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
+                                               ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [i32]
     return lib
 
 
-lib = _load()
+_handle = None
+
+
+def _lib() -> ctypes.CDLL:
+    """The library, loaded on first use (the builder imports this package
+    before any library exists); raises ImportError when it is not built."""
+    global _handle
+    if _handle is None:
+        _handle = _load()
+    return _handle
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
 
 
 def lora_status_string(status: int) -> str:
-    return lib.lora_status_string(int(status)).decode()
+    return _lib().lora_status_string(int(status)).decode()
 
 
 def _check(st: int, where: str) -> None:
@@ -116,12 +134,12 @@ def _ptr_array(tensors) -> ctypes.Array:
 
 
 def lora_meta_bytes(max_loras: int, max_num_tokens: int) -> int:
-    return int(lib.lora_meta_bytes(int(max_loras), int(max_num_tokens)))
+    return int(_lib().lora_meta_bytes(int(max_loras), int(max_num_tokens)))
 
 
 def lora_meta_bind(dev_ptr: int, nbytes: int, max_loras: int, max_num_tokens: int) -> lora_meta_t:
     m = lora_meta_t()
-    _check(lib.lora_meta_bind(dev_ptr, nbytes, int(max_loras), int(max_num_tokens), ctypes.byref(m)),
+    _check(_lib().lora_meta_bind(dev_ptr, nbytes, int(max_loras), int(max_num_tokens), ctypes.byref(m)),
            "lora_meta_bind")
     return m
 
@@ -135,8 +153,9 @@ class LoraMeta:
         nbytes = lora_meta_bytes(max_loras, max_num_tokens)
         if nbytes == 0:
             raise LoraError(LORA_ERR_MAX_LORAS, "lora_meta_bytes")
-        # torch's caching allocator returns 512-byte aligned blocks
-        self.region = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # torch's caching allocator returns 512-byte aligned blocks; zero-filled
+        # once so that the fused calls' counters start at zero
+        self.region = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         self.struct = lora_meta_bind(self.region.data_ptr(), nbytes, max_loras, max_num_tokens)
         self.max_loras, self.max_num_tokens = max_loras, max_num_tokens
 
@@ -164,7 +183,7 @@ class LoraMeta:
 def lora_prepare_meta(mapping, meta: LoraMeta, stream=None) -> None:
     """mapping: int32 device tensor [N] of LoRA ids (-1 = none)."""
     n = mapping.numel()
-    _check(lib.lora_prepare_meta(mapping.data_ptr() if n else None, n, ctypes.byref(meta.struct),
+    _check(_lib().lora_prepare_meta(mapping.data_ptr() if n else None, n, ctypes.byref(meta.struct),
                                  _stream(stream)), "lora_prepare_meta")
 
 
@@ -175,7 +194,7 @@ def lora_shrink(x, lora_a: Sequence, buf, meta: LoraMeta, scale: float, stream=N
     n, h = x.shape
     r = lora_a[0].shape[1]
     ptrs = _ptr_array(lora_a)
-    _check(lib.lora_shrink(x.data_ptr(), x.stride(0), n, h, ptrs, len(lora_a), r, buf.data_ptr(),
+    _check(_lib().lora_shrink(x.data_ptr(), x.stride(0), n, h, ptrs, len(lora_a), r, buf.data_ptr(),
                            ctypes.byref(meta.struct), float(scale), _stream(stream)), "lora_shrink")
 
 
@@ -188,7 +207,7 @@ def lora_expand(buf, lora_b: Sequence, bias: Optional[Sequence], y, meta: LoraMe
     widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
     bptrs = _ptr_array(lora_b)
     biasptrs = None if bias is None else _ptr_array(bias)
-    _check(lib.lora_expand(buf.data_ptr(), n, r, bptrs, biasptrs, widths, s, y.data_ptr(), y.stride(0),
+    _check(_lib().lora_expand(buf.data_ptr(), n, r, bptrs, biasptrs, widths, s, y.data_ptr(), y.stride(0),
                            int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
                            _stream(stream)), "lora_expand")
 
@@ -202,7 +221,24 @@ def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Seq
     s, _, r = buf.shape
     widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
     biasptrs = None if bias is None else _ptr_array(bias)
-    _check(lib.lora_shrink_expand(x.data_ptr(), x.stride(0), n, h, _ptr_array(lora_a), _ptr_array(lora_b),
+    _check(_lib().lora_shrink_expand(x.data_ptr(), x.stride(0), n, h, _ptr_array(lora_a), _ptr_array(lora_b),
                                   biasptrs, widths, s, r, buf.data_ptr(), y.data_ptr(), y.stride(0),
                                   int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
                                   float(scale), _stream(stream)), "lora_shrink_expand")
+
+
+def lora_prepare_shrink_expand(mapping, x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], buf, y,
+                               meta: LoraMeta, scale: float, offset_start: int = 0, add_inputs: bool = True,
+                               stream=None) -> None:
+    """lora_prepare_meta(mapping) then lora_shrink_expand, in one call (one
+    launch for small decode-like batches)."""
+    n = mapping.numel()
+    _, h = x.shape
+    s, _, r = buf.shape
+    widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
+    biasptrs = None if bias is None else _ptr_array(bias)
+    _check(_lib().lora_prepare_shrink_expand(mapping.data_ptr() if n else None, n, x.data_ptr(), x.stride(0), h,
+                                          _ptr_array(lora_a), _ptr_array(lora_b), biasptrs, widths, s, r,
+                                          buf.data_ptr(), y.data_ptr(), y.stride(0), int(offset_start),
+                                          int(bool(add_inputs)), ctypes.byref(meta.struct), float(scale),
+                                          _stream(stream)), "lora_prepare_shrink_expand")

@@ -140,12 +140,11 @@ int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, l
     return LORA_OK;
 }
 
-int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta, hipStream_t stream) {
-    int st = check_meta(meta);
-    if (st) return st;
-    if (num_tokens < 0 || num_tokens > meta->max_num_tokens) return LORA_ERR_NUM_TOKENS;
-    if (num_tokens > 0 && !mapping) return LORA_ERR_NULL;
+}  // extern "C"
 
+namespace {
+
+PrepareArgs prepare_args(const int32_t *mapping, int num_tokens, const lora_meta_t *meta) {
     PrepareArgs a;
     a.mapping = mapping;
     a.mapping_copy = meta->token_lora_mapping;
@@ -159,12 +158,29 @@ int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta,
     a.sync_tiles = num_tokens <= kFusedMaxTokens ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
     a.num_tokens = num_tokens;
     a.max_loras = meta->max_loras;
-    if (launch_prepare(a, stream) != hipSuccess) return LORA_ERR_LAUNCH;
-    if (meta->host_no_lora) {
-        if (hipMemcpyAsync(meta->host_no_lora, meta->no_lora_flag, sizeof(int32_t), hipMemcpyDeviceToHost,
-                           stream) != hipSuccess)
-            return LORA_ERR_LAUNCH;
-    }
+    return a;
+}
+
+// The optional host copy of the no-LoRA flag, after a prepare on `stream`.
+int mirror_flag(const lora_meta_t *meta, hipStream_t stream) {
+    if (meta->host_no_lora &&
+        hipMemcpyAsync(meta->host_no_lora, meta->no_lora_flag, sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+            hipSuccess)
+        return LORA_ERR_LAUNCH;
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta, hipStream_t stream) {
+    int st = check_meta(meta);
+    if (st) return st;
+    if (num_tokens < 0 || num_tokens > meta->max_num_tokens) return LORA_ERR_NUM_TOKENS;
+    if (num_tokens > 0 && !mapping) return LORA_ERR_NULL;
+    if (launch_prepare(prepare_args(mapping, num_tokens, meta), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    if ((st = mirror_flag(meta, stream))) return st;
     meta->num_tokens = num_tokens;
     return LORA_OK;
 }
@@ -326,6 +342,41 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
     if (launch_shrink(sa, shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     if (launch_expand(ea, expand_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
+}
+
+int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const void *x, int64_t ldx, int hidden,
+                               const void *const *lora_a, const void *const *lora_b, const void *const *bias,
+                               const int *slice_widths, int num_slices, int rank, float *buf, void *y,
+                               int64_t ldy, int offset_start, int add_inputs, lora_meta_t *meta, float scale,
+                               hipStream_t stream) {
+    int st = check_meta(meta);
+    if (st) return st;
+    if (num_tokens < 0 || num_tokens > meta->max_num_tokens) return LORA_ERR_NUM_TOKENS;
+    if (num_tokens > 0 && !mapping) return LORA_ERR_NULL;
+    // the layer's arguments are checked against the batch about to be prepared
+    lora_meta_t m = *meta;
+    m.num_tokens = num_tokens;
+    ShrinkArgs sa;
+    ExpandArgs ea;
+    bool skip = false;
+    if ((st = shrink_args(x, ldx, num_tokens, hidden, lora_a, num_slices, rank, buf, &m, scale, sa, skip))) return st;
+    if ((st = expand_args(buf, num_tokens, rank, lora_b, bias, slice_widths, num_slices, y, ldy, offset_start,
+                          add_inputs, &m, ea, skip)))
+        return st;
+    if (!skip && env_int("LORA_FUSED") >= 0) {
+        const int help = getenv("LORA_FUSED_HELP_AFTER") ? env_int("LORA_FUSED_HELP_AFTER") : 128;
+        const hipError_t e = launch_prepare_fused(prepare_args(mapping, num_tokens, meta), sa, ea, meta->sync,
+                                                  meta->status, help, env_int("LORA_FUSED_OWNERS_SKIP"), stream);
+        if (e == hipSuccess) {
+            if ((st = mirror_flag(meta, stream))) return st;
+            meta->num_tokens = num_tokens;
+            return LORA_OK;
+        }
+        if (e != hipErrorNotSupported) return LORA_ERR_LAUNCH;
+    }
+    if ((st = lora_prepare_meta(mapping, num_tokens, meta, stream))) return st;
+    return lora_shrink_expand(x, ldx, num_tokens, hidden, lora_a, lora_b, bias, slice_widths, num_slices, rank, buf,
+                              y, ldy, offset_start, add_inputs, meta, scale, stream);
 }
 
 const char *lora_status_string(int status) {

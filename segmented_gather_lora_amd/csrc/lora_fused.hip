@@ -45,6 +45,7 @@ namespace lora {
 struct FusedArgs {
     ShrinkArgs s;
     ExpandArgs e;
+    PrepareArgs p;          // the batch's mapping and metadata outputs (PREP kernels)
     int32_t *sync;
     int32_t *status;
     int32_t blocks;         // expand column blocks per tile (all slices)
@@ -86,9 +87,177 @@ __device__ __forceinline__ void reset_tile(int32_t *words, int parts) {
     for (int p = 0; p < parts; ++p) __hip_atomic_store(words + kFusedFlags + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LoRAKernelMeta._reset + prepare_tensors ("lora_kernel_metadata" page) for a
+// batch of at most kPrepMaxTokens tokens inside one workgroup of kThreads: the
+// stable counting sort of the prepare kernel (each wave ranks the tokens of its
+// contiguous slice with match masks and per-wave LDS counts; a scan over the
+// keys gives segment starts and slice bases; every token is placed at
+// base + rank), with 4 waves instead of 16.  The results land where
+// build_tile_table leaves them -- the tile table of `tile_tokens`-token tiles
+// followed by the sorted indices -- so the rest of the kernel is unchanged.
+// Workgroup `writer` also writes the metadata arrays, exactly as the prepare
+// kernel does.  Returns the number of tiles (0 for a no-LoRA batch).
+constexpr int kPrepMaxTokens = 2048;
+
+__device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, int *s_scan, int *s_flag,
+                              bool writer) {
+    constexpr int kSteps = kPrepMaxTokens / (kThreads);   // 64-token steps per wave at most
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int n = p.num_tokens;
+    const int nkeys = p.max_loras + 1;   // = slots
+    const int nbits = 32 - __clz(nkeys - 1);
+    int *pre = smem, *sid = pre + nkeys + 1, *sst = sid + nkeys, *scn = sst + nkeys;
+    int *ssorted = scn + nkeys;
+    int *cnt = ssorted + n;   // [key][wave]: running counts, then slice bases
+
+    for (int k = tid; k < nkeys * kWaves; k += kThreads) cnt[k] = 0;
+    if (tid == 0) {
+        s_flag[0] = 0;   // any id other than -1
+        s_flag[1] = 0;   // an id out of range
+    }
+    const int steps = (n + kWaves * kWave - 1) / (kWaves * kWave);
+    const int t0 = wave * steps * kWave;
+    int ids[kSteps];
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {   // one round trip (addresses clamped)
+        const int t = t0 + q * kWave + lane;
+        ids[q] = p.mapping[t < n ? t : n - 1];
+    }
+    __syncthreads();
+
+    // ---- 1. ranks within the wave's slice
+    int keys[kSteps], ranks[kSteps];
+    bool any = false, bad = false;
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+        keys[q] = 0;
+        ranks[q] = 0;
+        if (q >= steps) continue;   // uniform
+        const int t = t0 + q * kWave + lane;
+        const bool valid = t < n;
+        int id = valid ? ids[q] : -1;
+        if (id < -1 || id >= p.max_loras) {
+            bad = true;
+            id = -1;
+        }
+        const int key = id + 1;
+        any |= valid && id != -1;
+        const uint64_t m = match_key(key, valid, nbits);
+        const bool leader = valid && (m & lanemask_lt()) == 0;
+        keys[q] = key;
+        ranks[q] = cnt[key * kWaves + wave] + __popcll(m & lanemask_lt());
+        if (leader) cnt[key * kWaves + wave] += __popcll(m);   // this wave's column only
+    }
+    if (ballot(any) && lane == 0) atomicOr(&s_flag[0], 1);
+    if (ballot(bad) && lane == 0) atomicOr(&s_flag[1], 1);
+    __syncthreads();
+    const bool no_lora = s_flag[0] == 0;
+
+    // ---- 2. per key (contiguous keys per thread): count, non-empty, tiles; one scan of the three
+    const int per = (nkeys + kThreads - 1) / kThreads;   // <= 4
+    const int beg = tid * per;
+    int c[4], tl[4], sc = 0, sne = 0, stl = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = beg + i;
+        c[i] = 0;
+        tl[i] = 0;
+        if (i < per && k < nkeys) {
+            for (int w = 0; w < kWaves; ++w) c[i] += cnt[k * kWaves + w];
+            tl[i] = (k >= 1 && c[i] > 0 && !no_lora) ? (c[i] + tile_tokens - 1) / tile_tokens : 0;
+        }
+        sc += c[i];
+        sne += c[i] > 0 ? 1 : 0;
+        stl += tl[i];
+    }
+    const int ic = wave_inclusive_scan(sc), ine = wave_inclusive_scan(sne), itl = wave_inclusive_scan(stl);
+    if (lane == kWave - 1) {
+        s_scan[wave] = ic;
+        s_scan[kWaves + wave] = ine;
+        s_scan[2 * kWaves + wave] = itl;
+    }
+    __syncthreads();
+    int start = ic - sc, slot = ine - sne, tpre = itl - stl, n_active = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        start += w < wave ? s_scan[w] : 0;
+        slot += w < wave ? s_scan[kWaves + w] : 0;
+        tpre += w < wave ? s_scan[2 * kWaves + w] : 0;
+        n_active += s_scan[kWaves + w];
+        total += s_scan[2 * kWaves + w];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = beg + i;
+        if (i < per && k < nkeys) {
+            if (c[i] > 0) {
+                sid[slot] = k - 1;
+                scn[slot] = c[i];
+                sst[slot] = tl[i] ? start : 0;
+                pre[slot] = tpre;
+                if (writer && !no_lora) {
+                    p.active_ids[slot] = k - 1;
+                    p.counts[slot] = c[i];
+                    p.start_loc[slot + 1] = start + c[i];
+                }
+                ++slot;
+            }
+            int run = start;
+            for (int w = 0; w < kWaves; ++w) {
+                const int v = cnt[k * kWaves + w];
+                cnt[k * kWaves + w] = run;
+                run += v;
+            }
+            start += c[i];
+            tpre += tl[i];
+        }
+    }
+    // padding slots own no tiles; the metadata gets the _reset values there
+    for (int k = tid; k < nkeys; k += kThreads) {
+        if (k >= n_active) {
+            sid[k] = -1;
+            scn[k] = 0;
+            sst[k] = 0;
+            pre[k] = total;
+        }
+        if (writer && (no_lora || k >= n_active)) {
+            p.active_ids[k] = -1;
+            p.counts[k] = 0;
+        }
+    }
+    if (writer)
+        for (int k = tid; k < nkeys + 1; k += kThreads)
+            if (no_lora || k == 0 || k > n_active) p.start_loc[k] = 0;
+    if (tid == 0) {
+        pre[nkeys] = total;
+        if (writer) {
+            *p.no_lora = no_lora ? 1 : 0;
+            *p.status = s_flag[1] ? LORA_ERR_ID_RANGE : 0;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. stable scatter into LDS (and the metadata's copies)
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+        const int t = t0 + q * kWave + lane;
+        if (q < steps && t < n) {
+            const int pos = cnt[keys[q] * kWaves + wave] + ranks[q];
+            ssorted[pos] = t;
+            if (writer && !no_lora) {
+                p.sorted[pos] = t;
+                p.mapping_copy[t] = keys[q] - 1;
+            }
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
 // MT: 16-row tiles of weight rows (S*r <= 16*MT); KS: 32-wide K steps of the
-// expand (rank <= 32*KS).
-template <int MT, int KS, bool ADD>
+// expand (rank <= 32*KS); PREP: the kernel also prepares the batch (the tile
+// table comes from the mapping instead of the metadata).
+template <int MT, int KS, bool ADD, bool PREP>
 __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
     constexpr int kRowK = 32 * KS;
     constexpr int kRowStride = kRowK + 8;
@@ -109,7 +278,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
     const int rank = a.rank;
 
     const int nslots = a.meta.nslots;
-    const int total = build_tile_table<kThreads>(a.meta, kTile, smem, s_wsum);
+    __shared__ int s_scan[3 * kWaves], s_flag[2];
+    const int total = PREP ? prepare_in_lds(f.p, kTile, smem, s_scan, s_flag, blockIdx.x == 0)
+                           : build_tile_table<kThreads>(a.meta, kTile, smem, s_wsum);
     if (total == 0) return;
     const int grid = gridDim.x, b = blockIdx.x;
     // this workgroup's tiles: one tile shared by W workgroups, or every grid-th tile alone
@@ -433,38 +604,42 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
 
 typedef void (*FusedFn)(FusedArgs);
 
-template <int MT>
+template <int MT, bool PREP>
 FusedFn pick_ks(int ks, bool add) {
-    if (ks == 1) return add ? fused_kernel<MT, 1, true> : fused_kernel<MT, 1, false>;
-    return add ? fused_kernel<MT, 2, true> : fused_kernel<MT, 2, false>;
+    if (ks == 1) return add ? fused_kernel<MT, 1, true, PREP> : fused_kernel<MT, 1, false, PREP>;
+    return add ? fused_kernel<MT, 2, true, PREP> : fused_kernel<MT, 2, false, PREP>;
 }
 
+template <bool PREP>
 FusedFn pick(int mt, int ks, bool add) {
     switch (mt) {
-        case 1: return pick_ks<1>(ks, add);
-        case 2: return pick_ks<2>(ks, add);
-        case 3: return pick_ks<3>(ks, add);
-        default: return pick_ks<4>(ks, add);
+        case 1: return pick_ks<1, PREP>(ks, add);
+        case 2: return pick_ks<2, PREP>(ks, add);
+        case 3: return pick_ks<3, PREP>(ks, add);
+        default: return pick_ks<4, PREP>(ks, add);
     }
 }
 
 }  // namespace
 
-// Range: expected tokens per segment below 24, S * rank <= 64, rank <= 64.
-// K is split into chunks of 64-multiples until about 256 shrink parts exist,
-// as for the direct shrink kernel; the grid is what the device holds at once.
-hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *sync, int32_t *status,
-                        int help_after, int owners_skip, hipStream_t stream) {
+// Range: expected tokens per segment below 24, S * rank <= 64, rank <= 64
+// (and, with a prepare, at most kPrepMaxTokens tokens).  K is split into
+// chunks of 64-multiples until about 256 shrink parts exist, as for the direct
+// shrink kernel; the grid is what the device holds at once.
+static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const PrepareArgs *prep, int32_t *sync,
+                         int32_t *status, int help_after, int owners_skip, hipStream_t stream) {
     const int n = sin.num_tokens;
     const int nslots = sin.meta.nslots;
     const int segs = nslots < n ? nslots : n;
     const int avg = (n + segs - 1) / segs;
     if (avg >= 24 || n > kFusedMaxTokens || sin.rows > 64 || sin.rank > 64) return hipErrorNotSupported;
+    if (prep && n > kPrepMaxTokens) return hipErrorNotSupported;
 
     FusedArgs f;
     memset(&f, 0, sizeof f);
     f.s = sin;
     f.e = ein;
+    if (prep) f.p = *prep;
     f.sync = sync;
     f.status = status;
     f.help_after = help_after;
@@ -490,12 +665,15 @@ hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *s
     f.s.k_chunk = chunk;
     f.s.row_blocks = 1;
     f.s.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
+    if (prep) f.s.meta.lds_tokens = n;   // the kernel sorts into LDS itself
     f.e.meta.lds_tokens = f.s.meta.lds_tokens;
 
     const int mt = (sin.rows + 15) / 16;
     const int kse = (sin.rank + 31) / 32;
-    const FusedFn fn = pick(mt, kse, ein.add_inputs != 0);
-    const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + f.s.meta.lds_tokens);
+    const bool add = ein.add_inputs != 0;
+    const FusedFn fn = prep ? pick<true>(mt, kse, add) : pick<false>(mt, kse, add);
+    size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + f.s.meta.lds_tokens);
+    if (prep) lds += sizeof(int) * (size_t)nslots * kWaves;   // the sort's per-wave counts
     // enough workgroups for every tile's parts and blocks, at most what is resident
     const long tiles_upper = (n + kTile - 1) / kTile + segs;
     long grid = resident_grid(reinterpret_cast<const void *>(fn), kThreads, lds);
@@ -505,6 +683,17 @@ hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *s
     if (grid < kNumXcd) grid = kNumXcd;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, stream, f);
     return hipGetLastError();
+}
+
+hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *sync, int32_t *status,
+                        int help_after, int owners_skip, hipStream_t stream) {
+    return launch(sin, ein, nullptr, sync, status, help_after, owners_skip, stream);
+}
+
+hipError_t launch_prepare_fused(const PrepareArgs &prep, const ShrinkArgs &sin, const ExpandArgs &ein,
+                                int32_t *sync, int32_t *status, int help_after, int owners_skip,
+                                hipStream_t stream) {
+    return launch(sin, ein, &prep, sync, status, help_after, owners_skip, stream);
 }
 
 }  // namespace lora

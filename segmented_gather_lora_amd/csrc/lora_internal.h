@@ -326,6 +326,10 @@ hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream
 // caller then launches shrink and expand.
 hipError_t launch_fused(const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync, int32_t *status,
                         int help_after, int owners_skip, hipStream_t stream);
+// The same with the batch's prepare done inside the launch (at most 2048
+// tokens); hipErrorNotSupported likewise.
+hipError_t launch_prepare_fused(const PrepareArgs &p, const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync,
+                                int32_t *status, int help_after, int owners_skip, hipStream_t stream);
 
 // The fused call serves batches of short segments only: fewer than 24
 // tokens per LoRA on average, so at most kFusedMaxTokens tokens.

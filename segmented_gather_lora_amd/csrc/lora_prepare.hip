@@ -62,9 +62,14 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     }
     // the fused call's counters start every batch at zero (each fused call
     // also leaves them zero)
-    for (int k = tid; k < a.sync_tiles * (2 + kFusedMaxParts); k += kThreads) {
-        const int tile = k / (2 + kFusedMaxParts), w = k % (2 + kFusedMaxParts);
-        a.sync[kFusedTileWords * tile + (w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + w - 2)] = 0;
+    {   // per tile: the 16-byte groups holding the exit count, the done count and the part flags
+        constexpr int kGroups = 2 + kFusedMaxParts / 4;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int k = tid; k < a.sync_tiles * kGroups; k += kThreads) {
+            const int tile = k / kGroups, w = k % kGroups;
+            const int word = w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + 4 * (w - 2);
+            *reinterpret_cast<u32x4 *>(a.sync + kFusedTileWords * tile + word) = z;
+        }
     }
     __syncthreads();
 

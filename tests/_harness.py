@@ -180,18 +180,35 @@ def expand_check(y_gpu: np.ndarray, y_ref: np.ndarray, y0: np.ndarray, mag: np.n
     return dict(ratio=ratio, literal_rel=rel, exact_frac=float((y_gpu == y_ref).mean()) if err.size else 1.0)
 
 
+def poison_meta(meta) -> None:
+    """Overwrite every metadata array (not the fused counters) with garbage."""
+    for k, v in meta.views().items():
+        if k != "sync":
+            v.fill_(-12345)
+
+
 def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int | None = None,
-                  seed: int = 0, offset_start: int = 0, ldy_extra: int = 0, fused: bool = False) -> dict:
+                  seed: int = 0, offset_start: int = 0, ldy_extra: int = 0, fused: bool = False,
+                  prep: bool = False) -> dict:
     """prepare + (shrink, expand) per layer on the GPU -- or the one
-    lora_shrink_expand call with `fused` -- with metadata, buffer and output
-    compared with the oracle (all tokens, or a seeded sample)."""
+    lora_shrink_expand call per layer with `fused`, and with `prep` the first
+    layer's call also prepares the batch (lora_prepare_shrink_expand, on
+    poisoned metadata) -- with metadata, buffer and output compared with the
+    oracle (all tokens, or a seeded sample)."""
     sgl = lib()
     mapping = wl.mapping.numpy()
     n, ml = mapping.size, wl.spec.max_loras
     meta = sgl.LoraMeta(ml, max(n, 1))
-    sgl.lora_prepare_meta(wl.mapping.to("cuda"), meta)
-    torch.cuda.synchronize()
-    check_meta(meta, mapping, ml)
+    mapping_dev = wl.mapping.to("cuda")
+    if prep:
+        fused = True
+        poison_meta(meta)
+    else:
+        sgl.lora_prepare_meta(mapping_dev, meta)
+        torch.cuda.synchronize()
+        check_meta(meta, mapping, ml)
+    # ids outside [-1, max_loras) are reported by prepare and count as -1
+    mapping = np.where((mapping < -1) | (mapping >= ml), -1, mapping).astype(np.int32)
     tokens = np.arange(n, dtype=np.int32) if sample is None else sample_tokens(mapping, sample, seed)
     neg = mapping == -1
     stats = dict(shrink_ratio=0.0, expand_ratio=0.0, literal_rel=0.0)
@@ -214,7 +231,13 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
             y0full[:, :offset_start] = fill[:, :offset_start]
             y0full[:, offset_start + O:] = fill[:, offset_start + O:]
         y = y0full.to("cuda")
-        if fused and not sp.expand_only:
+        if prep and not sp.expand_only:
+            sgl.lora_prepare_shrink_expand(mapping_dev, D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale,
+                                           offset_start=offset_start, add_inputs=add_inputs)
+            torch.cuda.synchronize()
+            check_meta(meta, wl.mapping.numpy(), ml)
+            prep = False
+        elif fused and not sp.expand_only:
             sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale, offset_start=offset_start,
                                    add_inputs=add_inputs)
         else:

@@ -550,3 +550,105 @@ def test_fused_helping_path(name, n, mode, monkeypatch):
     wl = workloads.make_workload(name, num_tokens=n)
     print("fused helping", name, mode, flush=True)
     H.run_and_check(wl, add_inputs=True, fused=True)
+
+
+# ------------------------------------------------------------------ prepare + fused shrink -> expand
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+@pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("decode", 37), ("logits", None),
+                                    ("zipf", 300), ("large", 160), ("prefill", 600)])
+def test_prepare_fused_parity(name, n, add_inputs):
+    """lora_prepare_shrink_expand on poisoned metadata: the metadata written by
+    the one launch is bit-exact and buf / y match the oracle on every token
+    (the Zipf batch's second layer then uses lora_shrink_expand; rank 128 and
+    prefill take the separate calls)."""
+    wl = workloads.make_workload(name, num_tokens=n)
+    print("prepare+fused", name, n, add_inputs, flush=True)
+    print(H.run_and_check(wl, add_inputs=add_inputs, prep=True), flush=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=601, n=1, hidden=64, slices=(8,), rank=8, max_loras=1, neg_fraction=0.0),
+    dict(seed=602, n=2048, hidden=256, slices=(64, 64), rank=16, max_loras=1023, neg_fraction=0.1),
+    dict(seed=603, n=700, hidden=1032, slices=(264, 8, 520), rank=16, max_loras=200, bias=True),
+    dict(seed=604, n=2049, hidden=128, slices=(128,), rank=32, max_loras=500),
+    dict(seed=605, n=255, hidden=4104, slices=(512, 256), rank=32, max_loras=63, neg_fraction=0.95),
+])
+def test_prepare_fused_edge_shapes(case):
+    """One token; 2048 tokens over 1023 LoRAs (the largest one-launch batch,
+    every key slot used by the sort); 2049 tokens (the two calls); bias and
+    an offset; a batch that is almost all -1."""
+    wl = workloads.random_case(**case)
+    print("prepare+fused edge", case["seed"], flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=True)
+
+
+@pytest.mark.parametrize("kind", ["no_lora", "bad_ids"])
+def test_prepare_fused_special_batches(kind):
+    """An all -1 batch (no-LoRA flag, nothing touched) and ids out of range
+    (reported, treated as -1), through the one launch."""
+    sgl = H.lib()
+    wl = workloads.make_workload("decode", num_tokens=200)
+    m = wl.mapping.numpy().copy()
+    if kind == "no_lora":
+        m[:] = -1
+    else:
+        m[::7] = 32
+        m[3::11] = -5
+    wl.mapping.copy_(torch.from_numpy(m))
+    st = H.run_and_check(wl, add_inputs=True, prep=True)
+    print(kind, st, flush=True)
+
+
+def test_prepare_fused_graph_replay():
+    """One captured lora_prepare_shrink_expand replayed for several batches on
+    fixed buffers (one all -1), with eager work between replays; metadata and
+    results checked after every replay, and the host flag mirror."""
+    sgl = H.lib()
+    base = workloads.make_workload("decode")
+    L = base.layers[0]
+    sp = L.spec
+    n, ml = base.mapping.numel(), base.spec.max_loras
+    meta = sgl.LoraMeta(ml, n)
+    host_flag = torch.full((1,), -7, dtype=torch.int32, pin_memory=True)
+    meta.struct.host_no_lora = host_flag.data_ptr()
+    D = H.DevLayer(L)
+    mapping_dev = base.mapping.cuda()
+    buf = torch.zeros((3, n, sp.rank), dtype=torch.float32, device="cuda")
+    y = D.y0.clone()
+
+    def step():
+        sgl.lora_prepare_shrink_expand(mapping_dev, D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(43)
+    y0b = workloads.bf16_bits(L.y0)
+    tokens = np.arange(n, dtype=np.int32)
+    for rep in range(5):
+        m = rng.integers(-1, ml, n).astype(np.int32)
+        if rep == 1:
+            m[:] = -1
+        mapping_dev.copy_(torch.from_numpy(m))
+        buf.zero_()
+        y.copy_(D.y0)
+        H.poison_meta(meta)
+        torch.cuda.synchronize()
+        print("prepare+fused graph replay", rep, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        H.check_meta(meta, m, ml)
+        H.check_sync_clear(meta, n)
+        assert int(host_flag[0]) == (1 if rep == 1 else 0)
+        buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
+        buf_g, y_g = buf.cpu().numpy(), H.bits(y)
+        H.shrink_check(buf_g, buf_ref, bound)
+        H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
+    meta.struct.host_no_lora = None
