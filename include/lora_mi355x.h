@@ -199,11 +199,17 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
  * first LoRA layer (LoRAKernelMeta.prepare_tensors on the "lora_kernel_metadata"
  * page, then PunicaWrapperGPU.add_lora_linear on the "punica_gpu" page), with
  * the arguments and results of those two calls.  For batches of at most 2048
- * tokens in the fused call's range it is one launch: every workgroup sorts
- * the mapping in its own LDS (the same stable counting sort as
- * lora_prepare_meta) and workgroup 0 writes the metadata arrays.  Otherwise
- * the two calls are made.  As for lora_shrink_expand, meta must have been
- * prepared at least once since it was bound (its counters start at zero).
+ * tokens in the fused call's range it is one launch.  With at least 4 tokens
+ * per LoRA id (and every role resident at once) the launch is laid out by
+ * LoRA id: each workgroup picks its id's tokens out of the mapping itself
+ * (no sort; the tokens come in batch order, the stable sort's order within a
+ * segment) and the metadata arrays are written piecewise by each id's first
+ * expander.  Otherwise every workgroup sorts the mapping in its own LDS (the
+ * same stable counting sort as lora_prepare_meta) and workgroup 0 writes the
+ * metadata arrays.  Outside the range the two calls are made.  As for
+ * lora_shrink_expand, the counters in meta->sync must start at zero: meta
+ * must have been prepared since it was bound with at least as many tokens
+ * (or its region zeroed once when allocated); every call leaves them zero.
  * Records meta->num_tokens and copies the no-LoRA flag to meta->host_no_lora
  * when that is set.
  */

@@ -55,6 +55,7 @@ __device__ __forceinline__ int clamp_group(int c, int width) { return c < width 
 
 template <int KS, int TT, bool ADD, bool EARLY>
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
+    prefetch_kernargs<ExpandArgs>();
     constexpr int kUnitTokens = 16 * TT;
     constexpr int kRowK = 32 * KS;              // bf16 per staged row (rank padded to 32)
     constexpr int kRowStride = kRowK + 8;       // +16 bytes: rows start on different banks

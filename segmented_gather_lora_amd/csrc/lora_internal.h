@@ -54,6 +54,69 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// Touch every 64-byte line of a kernel's argument block at entry with scalar
+// loads issued together and waited for once, so that the scattered scalar
+// loads of the arguments later in the kernel hit the scalar cache instead of
+// each paying a memory round trip at its first use.  Only lines that lie
+// inside the block are touched.
+#define LORA_KA_LOAD(i, off) "s_load_dword %" #i ", %11, " #off "\n\t"
+#define LORA_KA_L1 LORA_KA_LOAD(0, 0x0)
+#define LORA_KA_L2 LORA_KA_L1 LORA_KA_LOAD(1, 0x40)
+#define LORA_KA_L3 LORA_KA_L2 LORA_KA_LOAD(2, 0x80)
+#define LORA_KA_L4 LORA_KA_L3 LORA_KA_LOAD(3, 0xc0)
+#define LORA_KA_L5 LORA_KA_L4 LORA_KA_LOAD(4, 0x100)
+#define LORA_KA_L6 LORA_KA_L5 LORA_KA_LOAD(5, 0x140)
+#define LORA_KA_L7 LORA_KA_L6 LORA_KA_LOAD(6, 0x180)
+#define LORA_KA_L8 LORA_KA_L7 LORA_KA_LOAD(7, 0x1c0)
+#define LORA_KA_L9 LORA_KA_L8 LORA_KA_LOAD(8, 0x200)
+#define LORA_KA_L10 LORA_KA_L9 LORA_KA_LOAD(9, 0x240)
+#define LORA_KA_L11 LORA_KA_L10 LORA_KA_LOAD(10, 0x280)
+#define LORA_KA_ASM(loads)                                                              \
+    asm volatile(loads "s_waitcnt lgkmcnt(0)"                                           \
+                 : "=&s"(d[0]), "=&s"(d[1]), "=&s"(d[2]), "=&s"(d[3]), "=&s"(d[4]),     \
+                   "=&s"(d[5]), "=&s"(d[6]), "=&s"(d[7]), "=&s"(d[8]), "=&s"(d[9]),     \
+                   "=&s"(d[10])                                                         \
+                 : "s"(k)                                                               \
+                 : "memory")
+
+template <typename Args>
+__device__ __forceinline__ void prefetch_kernargs() {
+    constexpr int lines = (int)((sizeof(Args) + 63) / 64);
+    static_assert(lines >= 1 && lines <= 11, "argument block larger than the prefetch covers");
+    auto k = __builtin_amdgcn_kernarg_segment_ptr();
+    int d[11];
+    if constexpr (lines == 1) LORA_KA_ASM(LORA_KA_L1);
+    else if constexpr (lines == 2) LORA_KA_ASM(LORA_KA_L2);
+    else if constexpr (lines == 3) LORA_KA_ASM(LORA_KA_L3);
+    else if constexpr (lines == 4) LORA_KA_ASM(LORA_KA_L4);
+    else if constexpr (lines == 5) LORA_KA_ASM(LORA_KA_L5);
+    else if constexpr (lines == 6) LORA_KA_ASM(LORA_KA_L6);
+    else if constexpr (lines == 7) LORA_KA_ASM(LORA_KA_L7);
+    else if constexpr (lines == 8) LORA_KA_ASM(LORA_KA_L8);
+    else if constexpr (lines == 9) LORA_KA_ASM(LORA_KA_L9);
+    else if constexpr (lines == 10) LORA_KA_ASM(LORA_KA_L10);
+    else LORA_KA_ASM(LORA_KA_L11);
+}
+
+// Pointer i of a kernel-argument pointer table, where i differs between
+// lanes.  Every entry is taken through readfirstlane, so the table is read
+// with scalar loads and the pick is a per-lane select; a plain p[i] would
+// become a per-lane gather from the argument block on the vector memory path,
+// whose wait also holds up every load issued before it.
+template <typename T, int N>
+__device__ __forceinline__ T *lane_slice_ptr(T *const (&p)[N], int i) {
+    T *r = nullptr;
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+        const uint64_t v = reinterpret_cast<uint64_t>(p[s]);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        T *ps = reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+        r = (s == 0 || i == s) ? ps : r;
+    }
+    return r;
+}
+
 // ---------------------------------------------------------------- bf16
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {

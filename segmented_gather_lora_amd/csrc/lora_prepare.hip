@@ -37,6 +37,7 @@ constexpr int kRankBits = 21;  // (key << 21) | rank: keys < 1024, ranks < 2^21 
 constexpr int kRankMask = (1 << kRankBits) - 1;
 
 __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
+    prefetch_kernargs<PrepareArgs>();
     // per key: the running count of each wave's slice (later its base)
     __shared__ __attribute__((aligned(16))) int s_cnt[kMaxKeys][kWaves];
     __shared__ int s_wa[kWaves], s_wb[kWaves];

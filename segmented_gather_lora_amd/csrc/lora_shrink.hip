@@ -34,10 +34,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ const uint16_t *select_ptr(const uint16_t *const (&p)[LORA_MAX_SLICES], int i) {
-    const uint16_t *r = p[0];
+template <typename T, int N>
+__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
+    T r = p[0];
 #pragma unroll
-    for (int s = 1; s < LORA_MAX_SLICES; ++s)
+    for (int s = 1; s < N; ++s)
         if (i == s) r = p[s];
     return r;
 }
@@ -70,6 +71,7 @@ __device__ __forceinline__ void mask_step(int kk, int kend, u32x4 (&v)[N][2]) {
 
 template <int NT, int MT, int WK>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
+    prefetch_kernargs<ShrinkArgs>();
     constexpr int WR = 4 / WK;
     constexpr int kTileTokens = 16 * NT;
     extern __shared__ int smem[];
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
             int row = rb * rows_per_wg + (wr * MT + mt) * 16 + col;
             row = row < a.rows ? row : a.rows - 1;
             const int i = row / a.rank, j = row - i * a.rank;
-            arow[mt] = select_ptr(a.a, i) + ((int64_t)tr.lora_id * a.rank + j) * a.hidden;
+            arow[mt] = select_slice(a.a, i) + ((int64_t)tr.lora_id * a.rank + j) * a.hidden;
         }
 
         const int kbeg = ks * a.k_chunk;
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
                 int row = rb * BR + (r - BT);
                 row = row < a.rows ? row : a.rows - 1;
                 const int i = row / a.rank, jr = row - i * a.rank;
-                src[j] = select_ptr(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
+                src[j] = select_slice(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
             }
         }
         auto issue = [&](int step, int buf) {

@@ -554,17 +554,67 @@ def test_fused_helping_path(name, n, mode, monkeypatch):
 
 # ------------------------------------------------------------------ prepare + fused shrink -> expand
 
+@pytest.mark.parametrize("layout", ["auto", "tile"])
 @pytest.mark.parametrize("add_inputs", [True, False])
 @pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("decode", 37), ("logits", None),
                                     ("zipf", 300), ("large", 160), ("prefill", 600)])
-def test_prepare_fused_parity(name, n, add_inputs):
+def test_prepare_fused_parity(name, n, add_inputs, layout, monkeypatch):
     """lora_prepare_shrink_expand on poisoned metadata: the metadata written by
     the one launch is bit-exact and buf / y match the oracle on every token
     (the Zipf batch's second layer then uses lora_shrink_expand; rank 128 and
-    prefill take the separate calls)."""
+    prefill take the separate calls).  "auto" takes the LoRA-major kernel for
+    decode, tiny, logits and the Zipf batch; "tile" forces the tile-major one."""
+    if layout == "tile":
+        monkeypatch.setenv("LORA_FUSED_LAYOUT", "tile")
     wl = workloads.make_workload(name, num_tokens=n)
-    print("prepare+fused", name, n, add_inputs, flush=True)
+    print("prepare+fused", name, n, add_inputs, layout, flush=True)
     print(H.run_and_check(wl, add_inputs=add_inputs, prep=True), flush=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=701, n=2000, hidden=1032, slices=(96, 40), rank=16, max_loras=100, bias=True),
+    dict(seed=702, n=512, hidden=4104, slices=(1024, 512, 512), rank=16, max_loras=32),
+    dict(seed=703, n=64, hidden=64, slices=(8,), rank=8, max_loras=16, neg_fraction=0.0),
+    dict(seed=704, n=300, hidden=8192, slices=(64,), rank=64, max_loras=24),
+    dict(seed=705, n=1000, hidden=512, slices=(24, 40, 8, 8, 8, 8, 8, 8), rank=8, max_loras=48, bias=True),
+])
+def test_lora_major_shapes(case, monkeypatch):
+    """The LoRA-major one-launch kernel (forced: the call fails if it does not
+    apply): about 20 tokens per id (two tiles each), ragged K over 9 parts,
+    exactly 4 tokens per id with a single part, rank 64 over 16 parts, eight
+    slices with bias, and an offset."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
+    wl = workloads.random_case(**case)
+    print("lora-major", case["seed"], flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=True)
+
+
+@pytest.mark.parametrize("add_inputs", [True, False])
+def test_lora_major_skewed_batch(add_inputs, monkeypatch):
+    """One id holding 300 of 512 tokens (19 tiles for its part owners and
+    expanders to walk) and every other id a few."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
+    wl = workloads.random_case(711, 512, 2048, (1024, 256, 256), 16, 32, neg_fraction=0.05)
+    m = wl.mapping.numpy().copy()
+    pos = np.random.default_rng(5).choice(512, 300, replace=False)
+    m[pos] = 5
+    wl.mapping.copy_(torch.from_numpy(m))
+    print("lora-major skewed", add_inputs, flush=True)
+    H.run_and_check(wl, add_inputs=add_inputs, prep=True)
+
+
+@pytest.mark.parametrize("layout", ["lora", "tile"])
+@pytest.mark.parametrize("mode", ["owners_skip", "help_at_once"])
+def test_prepare_fused_helping_path(mode, layout, monkeypatch):
+    """The waiters' fallback in both one-launch kernels, forced from the host
+    as for lora_shrink_expand."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", layout)
+    monkeypatch.setenv("LORA_FUSED_HELP_AFTER", "0")
+    if mode == "owners_skip":
+        monkeypatch.setenv("LORA_FUSED_OWNERS_SKIP", "1")
+    wl = workloads.make_workload("decode")
+    print("prepare+fused helping", mode, layout, flush=True)
+    H.run_and_check(wl, add_inputs=True, prep=True)
 
 
 @pytest.mark.parametrize("case", [
