@@ -233,8 +233,8 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
             name = r["Kernel_Name"]
             key = ("prepare" if "prepare_kernel" in name else "shrink" if "shrink_kernel" in name else
                    "expand" if "expand_kernel" in name else
-                   "preplinear" if "lora_major_kernel" in name else
-                   ("preplinear" if "true>" in name.split(",")[-1] else "linear") if "fused_kernel" in name else
+                   ("preplinear" if "true>" in name.split(",")[-1] else "linear")
+                   if ("fused_kernel" in name or "lora_major_kernel" in name) else
                    "copy" if ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()) else None)
             if key:
                 vals[key].append(float(r["Counter_Value"]) * 1024.0)

@@ -181,7 +181,10 @@ int lora_expand(const float *buf, int num_tokens, int rank,
  * the workgroups of each 16-token tile run its shrink parts, then wait on the
  * device until every part is done before their share of the tile's expand
  * (a waiter that sees no progress runs the parts nobody has started, so the
- * wait needs no co-residency).  Other shapes launch the two kernels.  The fused
+ * wait needs no co-residency).  With at least 4 tokens per LoRA id (and every
+ * role resident at once) the launch is laid out by LoRA id instead, reading
+ * the prepared id copy (token_lora_mapping) rather than the sorted indices.
+ * Other shapes launch the two kernels.  The fused
  * launch uses meta->sync; calls sharing one metadata region must not overlap
  * (they are ordered on one stream in normal use), and meta must have been
  * prepared at least once since it was bound.  Errors are those of the two

@@ -334,8 +334,8 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
         // test knobs: polls before a waiter helps (default 128), owners leaving
         // their parts to the waiters (forces the helping path)
         const int help = getenv("LORA_FUSED_HELP_AFTER") ? env_int("LORA_FUSED_HELP_AFTER") : 128;
-        const hipError_t e = launch_fused(sa, ea, meta->sync, meta->status, help, env_int("LORA_FUSED_OWNERS_SKIP"),
-                                          stream);
+        const hipError_t e = launch_fused(sa, ea, meta->token_lora_mapping, meta->max_loras, meta->sync, meta->status,
+                                          help, env_int("LORA_FUSED_OWNERS_SKIP"), stream);
         if (e == hipSuccess) return LORA_OK;
         if (e != hipErrorNotSupported) return LORA_ERR_LAUNCH;
     }

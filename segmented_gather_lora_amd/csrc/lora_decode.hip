@@ -172,7 +172,10 @@ __device__ void write_meta(const PrepareArgs &p, const Ids &ids, int n, int L, i
 template <int MT, int KS>
 constexpr int kLmWavesPerSimd = (KS == 1 && MT <= 3) ? 4 : 1;
 
-template <int MT, int KS, bool ADD>
+// PREP: the launch also prepares the batch (f.p.mapping is the raw mapping and
+// the metadata arrays are written); otherwise f.p.mapping is the prepared id
+// copy and the metadata is left alone.
+template <int MT, int KS, bool ADD, bool PREP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kLmWavesPerSimd<MT, KS>)))
 void lora_major_kernel(FusedArgs f) {
     extern __shared__ int smem[];
@@ -194,12 +197,15 @@ void lora_major_kernel(FusedArgs f) {
     const int nparts = a.k_splits;
     int *const s_list = smem;         // this id's tokens
     int *const s_list0 = smem + n;    // key-0 tokens (metadata only)
-    auto is_mine = [&](int id) { return id == L; };
 
     // the ids first: memory counters complete in order, so the token filter
-    // then waits for them only, not for the weights issued after them
+    // then waits for them only, not for the weights issued after them.  A
+    // prepared no-LoRA batch keeps the previous batch's id copy (prepare
+    // returns before copying), so without a prepare the flag decides.
     Ids ids;
     load_ids(f.p.mapping, n, ids);
+    const int no_lora = PREP ? 0 : *a.meta.no_lora;
+    auto mine = [&](int id) { return id == L && !no_lora; };
 
     int32_t *const words = f.sync + kFusedTileWords * L;
     int32_t *const parts_done = words + kFusedPartsDone;
@@ -235,7 +241,7 @@ void lora_major_kernel(FusedArgs f) {
                 }
             }
         }
-        const int cnt = pick_tokens<true>(ids, n, is_mine, s_list, s_wcnt);
+        const int cnt = pick_tokens<true>(ids, n, mine, s_list, s_wcnt);
         if (cnt == 0) return;   // the whole workgroup: no word of L is touched by anyone
         int got = 0;
         if (!f.owners_skip) {
@@ -357,7 +363,7 @@ void lora_major_kernel(FusedArgs f) {
     Block bk = block_at(e0);
     load_weights(bk);
 
-    const int cnt = pick_tokens<true>(ids, n, is_mine, s_list, s_wcnt);
+    const int cnt = pick_tokens<true>(ids, n, mine, s_list, s_wcnt);
     auto token_at = [&](int pidx) { return s_list[pidx < cnt ? pidx : cnt - 1]; };
     // y rows of tile `t` for the current block (no dependence on buf)
     u32x2 yv[4];
@@ -371,7 +377,7 @@ void lora_major_kernel(FusedArgs f) {
         }
     };
     if (cnt > 0) load_y(0);
-    if (e0 == 0 && (cnt > 0 || L == 0)) write_meta(f.p, ids, n, L, cnt, s_list, s_list0, s_wcnt, s_bits);
+    if (PREP && e0 == 0 && (cnt > 0 || L == 0)) write_meta(f.p, ids, n, L, cnt, s_list, s_list0, s_wcnt, s_bits);
     if (cnt == 0) return;   // the whole workgroup: no word of L is touched by anyone
     const int ntiles = (cnt + kTile - 1) / kTile;
 
@@ -506,18 +512,19 @@ void lora_major_kernel(FusedArgs f) {
 
 typedef void (*LoraMajorFn)(FusedArgs);
 
-template <int MT>
+template <int MT, bool PREP>
 LoraMajorFn pick_ks(int ks, bool add) {
-    if (ks == 1) return add ? lora_major_kernel<MT, 1, true> : lora_major_kernel<MT, 1, false>;
-    return add ? lora_major_kernel<MT, 2, true> : lora_major_kernel<MT, 2, false>;
+    if (ks == 1) return add ? lora_major_kernel<MT, 1, true, PREP> : lora_major_kernel<MT, 1, false, PREP>;
+    return add ? lora_major_kernel<MT, 2, true, PREP> : lora_major_kernel<MT, 2, false, PREP>;
 }
 
+template <bool PREP>
 LoraMajorFn pick(int mt, int ks, bool add) {
     switch (mt) {
-        case 1: return pick_ks<1>(ks, add);
-        case 2: return pick_ks<2>(ks, add);
-        case 3: return pick_ks<3>(ks, add);
-        default: return pick_ks<4>(ks, add);
+        case 1: return pick_ks<1, PREP>(ks, add);
+        case 2: return pick_ks<2, PREP>(ks, add);
+        case 3: return pick_ks<3, PREP>(ks, add);
+        default: return pick_ks<4, PREP>(ks, add);
     }
 }
 
@@ -529,8 +536,9 @@ LoraMajorFn pick(int mt, int ks, bool add) {
 // role of every id resident at once (max_loras * (parts + blocks) workgroups).
 // The counter words of id L are those of tile L, which the metadata region
 // holds for every id when the batch has more tokens than ids.
-hipError_t launch_lora_major(const FusedArgs &fin, int max_loras, hipStream_t stream) {
+hipError_t launch_lora_major(const FusedArgs &fin, bool prepare, hipStream_t stream) {
     const int n = fin.s.num_tokens;
+    const int max_loras = fin.p.max_loras;
     if (n > kPrepMaxTokens || n < 4 * max_loras || n <= max_loras) return hipErrorNotSupported;
     if (fin.s.rows > 64 || fin.s.rank > 64) return hipErrorNotSupported;
     FusedArgs f = fin;
@@ -548,8 +556,9 @@ hipError_t launch_lora_major(const FusedArgs &fin, int max_loras, hipStream_t st
 
     const int mt = (fin.s.rows + 15) / 16;
     const int kse = (fin.s.rank + 31) / 32;
-    const LoraMajorFn fn = pick(mt, kse, fin.e.add_inputs != 0);
-    const size_t lds = sizeof(int) * (size_t)(2 * n);   // the id's tokens, the key-0 tokens
+    const bool add = fin.e.add_inputs != 0;
+    const LoraMajorFn fn = prepare ? pick<true>(mt, kse, add) : pick<false>(mt, kse, add);
+    const size_t lds = sizeof(int) * (size_t)((prepare ? 2 : 1) * n);   // the id's tokens (, the key-0 tokens)
     const long grid = (long)max_loras * (parts + f.blocks);
     if (grid > resident_grid(reinterpret_cast<const void *>(fn), kThreads, lds)) return hipErrorNotSupported;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, stream, f);

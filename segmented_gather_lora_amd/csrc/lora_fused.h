@@ -223,7 +223,9 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
 }  // namespace
 
 // LoRA-major launch (lora_decode.hip): hipErrorNotSupported when the batch is
-// outside its range, so the caller can take the tile-major kernel.
-hipError_t launch_lora_major(const FusedArgs &f, int max_loras, hipStream_t stream);
+// outside its range, so the caller can take the tile-major kernel.  f.p holds
+// the batch's ids, count and max_loras; with `prepare` the launch also writes
+// the metadata arrays of f.p (its ids are then the raw mapping).
+hipError_t launch_lora_major(const FusedArgs &f, bool prepare, hipStream_t stream);
 
 }  // namespace lora

@@ -418,8 +418,9 @@ FusedFn pick(int mt, int ks, bool add) {
 // (and, with a prepare, at most kPrepMaxTokens tokens).  K is split into
 // chunks of 64-multiples until about 256 shrink parts exist, as for the direct
 // shrink kernel; the grid is what the device holds at once.
-static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const PrepareArgs *prep, int32_t *sync,
-                         int32_t *status, int help_after, int owners_skip, hipStream_t stream) {
+static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const PrepareArgs *prep,
+                         const int32_t *mapping_copy, int max_loras, int32_t *sync, int32_t *status, int help_after,
+                         int owners_skip, hipStream_t stream) {
     const int n = sin.num_tokens;
     const int nslots = sin.meta.nslots;
     const int segs = nslots < n ? nslots : n;
@@ -447,10 +448,16 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
     // batches with every LoRA id likely present: the LoRA-major kernel
     // (test and comparison knob LORA_FUSED_LAYOUT: "tile" keeps this kernel,
     // "lora" fails the launch when the LoRA-major kernel does not apply)
-    if (prep) {
+    {
         const char *layout = getenv("LORA_FUSED_LAYOUT");
         if (!layout || strcmp(layout, "tile") != 0) {
-            const hipError_t r = launch_lora_major(f, prep->max_loras, stream);
+            FusedArgs g = f;
+            if (!prep) {
+                g.p.mapping = mapping_copy;
+                g.p.num_tokens = n;
+                g.p.max_loras = max_loras;
+            }
+            const hipError_t r = launch_lora_major(g, prep != nullptr, stream);
             if (r != hipErrorNotSupported) return r;
             if (layout && strcmp(layout, "lora") == 0) return hipErrorInvalidValue;
         }
@@ -489,15 +496,15 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, int32_t *sync, int32_t *status,
-                        int help_after, int owners_skip, hipStream_t stream) {
-    return launch(sin, ein, nullptr, sync, status, help_after, owners_skip, stream);
+hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, const int32_t *mapping_copy, int max_loras,
+                        int32_t *sync, int32_t *status, int help_after, int owners_skip, hipStream_t stream) {
+    return launch(sin, ein, nullptr, mapping_copy, max_loras, sync, status, help_after, owners_skip, stream);
 }
 
 hipError_t launch_prepare_fused(const PrepareArgs &prep, const ShrinkArgs &sin, const ExpandArgs &ein,
                                 int32_t *sync, int32_t *status, int help_after, int owners_skip,
                                 hipStream_t stream) {
-    return launch(sin, ein, &prep, sync, status, help_after, owners_skip, stream);
+    return launch(sin, ein, &prep, nullptr, prep.max_loras, sync, status, help_after, owners_skip, stream);
 }
 
 }  // namespace lora

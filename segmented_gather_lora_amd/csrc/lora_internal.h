@@ -386,9 +386,11 @@ hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream
 hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream_t s);
 // Fused shrink -> expand for short segments.  Returns hipErrorNotSupported
 // (launching nothing) when the shape is outside the fused kernel's range; the
-// caller then launches shrink and expand.
-hipError_t launch_fused(const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync, int32_t *status,
-                        int help_after, int owners_skip, hipStream_t stream);
+// caller then launches shrink and expand.  `mapping_copy` is the prepared
+// batch's id copy (ids outside [-1, max_loras) already -1), read by the
+// LoRA-major layout.
+hipError_t launch_fused(const ShrinkArgs &s, const ExpandArgs &e, const int32_t *mapping_copy, int max_loras,
+                        int32_t *sync, int32_t *status, int help_after, int owners_skip, hipStream_t stream);
 // The same with the batch's prepare done inside the launch (at most 2048
 // tokens); hipErrorNotSupported likewise.
 hipError_t launch_prepare_fused(const PrepareArgs &p, const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync,

@@ -431,13 +431,17 @@ def test_graph_captured_decode_step():
 
 # ------------------------------------------------------------------ fused shrink -> expand
 
+@pytest.mark.parametrize("layout", ["auto", "tile"])
 @pytest.mark.parametrize("add_inputs", [True, False])
 @pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("decode", 37), ("logits", None),
                                     ("zipf", 300), ("prefill", 600), ("large", 160)])
-def test_fused_parity(name, n, add_inputs):
+def test_fused_parity(name, n, add_inputs, layout, monkeypatch):
     """lora_shrink_expand against the oracle on every token: one launch for the
-    decode-like shapes (decode, tiny, logits, a short Zipf batch), the two
-    kernels for the others (prefill, rank 128)."""
+    decode-like shapes (decode, tiny, logits, a short Zipf batch; LoRA-major
+    for decode, tiny and Zipf unless "tile" forces the tile-major kernel), the
+    two kernels for the others (prefill, rank 128)."""
+    if layout == "tile":
+        monkeypatch.setenv("LORA_FUSED_LAYOUT", "tile")
     wl = workloads.make_workload(name, num_tokens=n)
     print("fused", name, n, add_inputs, flush=True)
     print(H.run_and_check(wl, add_inputs=add_inputs, fused=True), flush=True)
@@ -537,13 +541,15 @@ def test_fused_graph_replay():
         H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
 
 
+@pytest.mark.parametrize("layout", ["lora", "tile"])
 @pytest.mark.parametrize("mode", ["owners_skip", "help_at_once"])
 @pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None)])
-def test_fused_helping_path(name, n, mode, monkeypatch):
+def test_fused_helping_path(name, n, mode, layout, monkeypatch):
     """The waiters' fallback, forced from the host: with owners leaving their
     parts, every part is run by waiters that take it by its flag; with no
     patience at all, owners and waiters race for every part.  Results and the
-    counters' reset must be the same as on the normal path."""
+    counters' reset must be the same as on the normal path, in both layouts."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", layout)
     monkeypatch.setenv("LORA_FUSED_HELP_AFTER", "0")
     if mode == "owners_skip":
         monkeypatch.setenv("LORA_FUSED_OWNERS_SKIP", "1")
@@ -578,29 +584,32 @@ def test_prepare_fused_parity(name, n, add_inputs, layout, monkeypatch):
     dict(seed=704, n=300, hidden=8192, slices=(64,), rank=64, max_loras=24),
     dict(seed=705, n=1000, hidden=512, slices=(24, 40, 8, 8, 8, 8, 8, 8), rank=8, max_loras=48, bias=True),
 ])
-def test_lora_major_shapes(case, monkeypatch):
+@pytest.mark.parametrize("prep", [True, False])
+def test_lora_major_shapes(case, prep, monkeypatch):
     """The LoRA-major one-launch kernel (forced: the call fails if it does not
-    apply): about 20 tokens per id (two tiles each), ragged K over 9 parts,
-    exactly 4 tokens per id with a single part, rank 64 over 16 parts, eight
-    slices with bias, and an offset."""
+    apply), with and without the prepare: about 20 tokens per id (two tiles
+    each), ragged K over 9 parts, exactly 4 tokens per id with a single part,
+    rank 64 over 16 parts, eight slices with bias, and an offset."""
     monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
     wl = workloads.random_case(**case)
-    print("lora-major", case["seed"], flush=True)
-    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=True)
+    print("lora-major", case["seed"], prep, flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=prep, fused=not prep)
 
 
+@pytest.mark.parametrize("prep", [True, False])
 @pytest.mark.parametrize("add_inputs", [True, False])
-def test_lora_major_skewed_batch(add_inputs, monkeypatch):
+def test_lora_major_skewed_batch(add_inputs, prep, monkeypatch):
     """One id holding 300 of 512 tokens (19 tiles for its part owners and
-    expanders to walk) and every other id a few."""
+    expanders to walk) and every other id a few, with and without the
+    prepare in the launch."""
     monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
     wl = workloads.random_case(711, 512, 2048, (1024, 256, 256), 16, 32, neg_fraction=0.05)
     m = wl.mapping.numpy().copy()
     pos = np.random.default_rng(5).choice(512, 300, replace=False)
     m[pos] = 5
     wl.mapping.copy_(torch.from_numpy(m))
-    print("lora-major skewed", add_inputs, flush=True)
-    H.run_and_check(wl, add_inputs=add_inputs, prep=True)
+    print("lora-major skewed", add_inputs, prep, flush=True)
+    H.run_and_check(wl, add_inputs=add_inputs, prep=prep, fused=not prep)
 
 
 @pytest.mark.parametrize("layout", ["lora", "tile"])
