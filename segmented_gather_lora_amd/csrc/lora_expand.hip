@@ -284,10 +284,13 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     const int nslots = a.meta.nslots;
     const int segs = nslots < n ? nslots : n;
     const int ks = (a.rank + 31) / 32;
+    const int avg = (n + segs - 1) / segs;
     int tt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : 4;
     if (cfg.tile_tokens <= 0) {
-        const int avg = (n + segs - 1) / segs;
         while (tt > 1 && 16 * tt / 2 >= avg) tt /= 2;
+        // up to rank 32, 32-token tiles measured faster than 64-token ones
+        // (twice the units over the same y traffic, little buffer per unit)
+        if (a.rank <= 32 && tt > 2) tt = 2;
     }
     tt = tt >= 4 ? 4 : (tt >= 2 ? 2 : 1);
     a.tile_tokens = 16 * tt;
@@ -305,14 +308,18 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
         for (int i = a.num_slices; i <= LORA_MAX_SLICES; ++i) a.run_begin[i] = (int)runs;
         return runs;
     };
+    // Run length: 16 blocks when segments are tiny (each unit then stages a
+    // handful of buffer rows once for many weight blocks), else 4; halved
+    // while fewer than kMinUnits units would be left to spread over the
+    // device.  Fitted to sweeps over the decode, prefill, Zipf, large, logits
+    // and embedding shapes.
+    constexpr long kMinUnits = 800;
     int r = 1;
     if (cfg.run_blocks > 0) {
         r = cfg.run_blocks;
     } else {
-        const long resident = resident_grid(reinterpret_cast<const void *>(pick(ks, tt, add, false)), kThreads, lds);
-        const bool few_units = tiles_upper * count_runs(1) <= 2 * resident;
-        const bool light_rows = tt == 4 && a.rank <= 16;   // little buffer to stage per unit
-        r = (few_units || light_rows) ? 1 : 4;
+        r = avg < 16 ? 16 : 4;
+        while (r > 1 && tiles_upper * count_runs(r) < kMinUnits) r /= 2;
     }
     a.run_blocks = r;
     a.runs = (int)count_runs(r);
