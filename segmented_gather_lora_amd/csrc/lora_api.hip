@@ -155,7 +155,7 @@ PrepareArgs prepare_args(const int32_t *mapping, int num_tokens, const lora_meta
     a.no_lora = meta->no_lora_flag;
     a.status = meta->status;
     a.sync = meta->sync;
-    a.sync_tiles = num_tokens <= kFusedMaxTokens ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
+    a.sync_tiles = fused_batch(num_tokens, meta->max_loras + 1) ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
     a.num_tokens = num_tokens;
     a.max_loras = meta->max_loras;
     return a;

@@ -64,7 +64,7 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
     const int nbits = 32 - __clz(nkeys - 1);
     int *pre = smem, *sid = pre + nkeys + 1, *sst = sid + nkeys, *scn = sst + nkeys;
     int *ssorted = scn + nkeys;
-    int *cnt = ssorted + n;   // [key][wave]: running counts, then slice bases
+    int *cnt = ssorted + n;   // [wave][key]: running counts, then slice bases (wave-major: no bank conflicts)
 
     for (int k = tid; k < nkeys * kWaves; k += kThreads) cnt[k] = 0;
     if (tid == 0) {
@@ -101,8 +101,8 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
         const uint64_t m = match_key(key, valid, nbits);
         const bool leader = valid && (m & lanemask_lt()) == 0;
         keys[q] = key;
-        ranks[q] = cnt[key * kWaves + wave] + __popcll(m & lanemask_lt());
-        if (leader) cnt[key * kWaves + wave] += __popcll(m);   // this wave's column only
+        ranks[q] = cnt[wave * nkeys + key] + __popcll(m & lanemask_lt());
+        if (leader) cnt[wave * nkeys + key] += __popcll(m);   // this wave's row only
     }
     if (ballot(any) && lane == 0) atomicOr(&s_flag[0], 1);
     if (ballot(bad) && lane == 0) atomicOr(&s_flag[1], 1);
@@ -119,7 +119,7 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
         c[i] = 0;
         tl[i] = 0;
         if (i < per && k < nkeys) {
-            for (int w = 0; w < kWaves; ++w) c[i] += cnt[k * kWaves + w];
+            for (int w = 0; w < kWaves; ++w) c[i] += cnt[w * nkeys + k];
             tl[i] = (k >= 1 && c[i] > 0 && !no_lora) ? (c[i] + tile_tokens - 1) / tile_tokens : 0;
         }
         sc += c[i];
@@ -160,8 +160,8 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
             }
             int run = start;
             for (int w = 0; w < kWaves; ++w) {
-                const int v = cnt[k * kWaves + w];
-                cnt[k * kWaves + w] = run;
+                const int v = cnt[w * nkeys + k];
+                cnt[w * nkeys + k] = run;
                 run += v;
             }
             start += c[i];
@@ -198,7 +198,7 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
     for (int q = 0; q < kSteps; ++q) {
         const int t = t0 + q * kWave + lane;
         if (q < steps && t < n) {
-            const int pos = cnt[keys[q] * kWaves + wave] + ranks[q];
+            const int pos = cnt[wave * nkeys + keys[q]] + ranks[q];
             ssorted[pos] = t;
             if (writer && !no_lora) {
                 p.sorted[pos] = t;
@@ -589,8 +589,7 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
     const int n = sin.num_tokens;
     const int nslots = sin.meta.nslots;
     const int segs = nslots < n ? nslots : n;
-    const int avg = (n + segs - 1) / segs;
-    if (avg >= 24 || n > kFusedMaxTokens || sin.rows > 64 || sin.rank > 64) return hipErrorNotSupported;
+    if (!fused_batch(n, nslots) || sin.rows > 64 || sin.rank > 64) return hipErrorNotSupported;
     if (prep && n > kPrepMaxTokens) return hipErrorNotSupported;
 
     FusedArgs f;

@@ -411,5 +411,13 @@ inline long fused_tiles(long n, long nslots) {
     return (n + 15) / 16 + (nslots < n ? nslots : n) + 1;
 }
 inline long fused_sync_words(long n, long nslots) { return kFusedTileWords * fused_tiles(n, nslots); }
+// Batches a fused call can take (by size alone): fewer than 24 tokens per
+// segment on average and at most kFusedMaxTokens tokens.  Only their
+// counters need zeroing by prepare.
+inline bool fused_batch(long n, long nslots) {
+    if (n < 1 || n > kFusedMaxTokens) return false;
+    const long segs = nslots < n ? nslots : n;
+    return (n + segs - 1) / segs < 24;
+}
 
 }  // namespace lora

@@ -15,7 +15,7 @@
 //      equal keys of a step are grouped with one ballot per key bit (match
 //      mask), a token's rank in the slice is the slice's running count of its
 //      key plus the popcount of the match mask below its lane, and one lane
-//      per group bumps the running count (an LDS column owned by the wave).
+//      per group bumps the running count (an LDS row owned by the wave).
 //   2. One thread per key adds up its 16 slice counts (the histogram), a
 //      block scan over the keys gives the segment starts and the compacted
 //      id list, and each key's 16 counts become 16 slice bases.
@@ -35,13 +35,20 @@ constexpr int kMaxKeys = LORA_MAX_LORAS + 1;
 constexpr int kSteps = 16;     // steps of 64 tokens per wave held in registers
 constexpr int kRankBits = 21;  // (key << 21) | rank: keys < 1024, ranks < 2^21 tokens
 constexpr int kRankMask = (1 << kRankBits) - 1;
+// Batches whose ranks stay in registers (kSteps steps of 64 tokens per wave)
+// also stage the sorted indices in LDS and write them out coalesced: a direct
+// scatter from one workgroup costs a partial cache-line write per token.
+constexpr int kLdsSorted = kSteps * kThreads;
 
 __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     prefetch_kernargs<PrepareArgs>();
-    // per key: the running count of each wave's slice (later its base)
-    __shared__ __attribute__((aligned(16))) int s_cnt[kMaxKeys][kWaves];
+    // per wave and key: the running count of the wave's slice (later its
+    // base).  Wave-major, so the lanes of a step, which hold different keys,
+    // reach different banks.
+    __shared__ __attribute__((aligned(16))) int s_cnt[kWaves][kMaxKeys];
     __shared__ int s_wa[kWaves], s_wb[kWaves];
     __shared__ int s_any, s_bad;
+    __shared__ __attribute__((aligned(16))) int s_sorted[kLdsSorted];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int n = a.num_tokens;
@@ -52,11 +59,7 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     const int t0 = wave * slice;
     const bool in_regs = steps <= kSteps;
 
-    {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int k = tid; k < nkeys * (kWaves / 4); k += kThreads)
-            reinterpret_cast<u32x4 *>(&s_cnt[0][0])[k] = z;
-    }
+    for (int k = tid; k < kWaves * nkeys; k += kThreads) s_cnt[k / nkeys][k % nkeys] = 0;
     if (tid == 0) {
         s_any = 0;
         s_bad = 0;
@@ -98,9 +101,9 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
             any |= valid && id != -1;
             const uint64_t m = match_key(key, valid, nbits);
             const bool leader = valid && (m & lanemask_lt()) == 0;
-            const int rank = s_cnt[key][wave] + __popcll(m & lanemask_lt());
+            const int rank = s_cnt[wave][key] + __popcll(m & lanemask_lt());
             packed[q] = (key << kRankBits) | rank;
-            if (leader) s_cnt[key][wave] += __popcll(m);   // this wave's column only
+            if (leader) s_cnt[wave][key] += __popcll(m);   // this wave's row only
         }
         if (!in_regs) {
 #pragma unroll
@@ -135,15 +138,10 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     int c = 0;
     if (tid < nkeys) {
 #pragma unroll
-        for (int v = 0; v < kWaves / 4; ++v) {
-            const u32x4 q4 = reinterpret_cast<const u32x4 *>(&s_cnt[tid][0])[v];
-            col[4 * v] = (int)q4[0];
-            col[4 * v + 1] = (int)q4[1];
-            col[4 * v + 2] = (int)q4[2];
-            col[4 * v + 3] = (int)q4[3];
+        for (int w = 0; w < kWaves; ++w) {
+            col[w] = s_cnt[w][tid];
+            c += col[w];
         }
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += col[w];
     }
     const int ne = c > 0 ? 1 : 0;
     const int ic = wave_inclusive_scan(c), ine = wave_inclusive_scan(ne);
@@ -168,14 +166,9 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     if (tid < nkeys) {
         int run = start;
 #pragma unroll
-        for (int v = 0; v < kWaves / 4; ++v) {
-            u32x4 q4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                q4[e] = (uint32_t)run;
-                run += col[4 * v + e];
-            }
-            reinterpret_cast<u32x4 *>(&s_cnt[tid][0])[v] = q4;
+        for (int w = 0; w < kWaves; ++w) {
+            s_cnt[w][tid] = run;
+            run += col[w];
         }
     }
     for (int k = tid; k < nkeys; k += kThreads) {
@@ -189,24 +182,32 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     __syncthreads();
 
     // ---- 3. stable scatter
-    if (in_regs) {
+    if (in_regs) {   // n <= kLdsSorted: into LDS, then one coalesced pass
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) {
             const int t = t0 + q * kWave + lane;
             if (q < steps && t < n) {
                 const int key = (int)((unsigned)packed[q] >> kRankBits), rank = packed[q] & kRankMask;
-                const int pos = s_cnt[key][wave] + rank;
-                if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
+                const int pos = s_cnt[wave][key] + rank;
+                if ((unsigned)pos < (unsigned)n) s_sorted[pos] = t;
                 a.mapping_copy[t] = key - 1;
             }
         }
+        __syncthreads();
+        int k0 = 0;
+        if ((reinterpret_cast<uintptr_t>(a.sorted) & 15) == 0) {
+            k0 = n & ~3;
+            for (int k = 4 * tid; k < k0; k += 4 * kThreads)
+                *reinterpret_cast<u32x4 *>(a.sorted + k) = *reinterpret_cast<const u32x4 *>(&s_sorted[k]);
+        }
+        for (int k = k0 + tid; k < n; k += kThreads) a.sorted[k] = s_sorted[k];
     } else {
         for (int s = 0; s < steps; ++s) {
             const int t = t0 + s * kWave + lane;
             if (t < n) {
                 const int v = a.mapping_copy[t];
                 const int key = (int)((unsigned)v >> kRankBits), rank = v & kRankMask;
-                const int pos = s_cnt[key][wave] + rank;
+                const int pos = s_cnt[wave][key] + rank;
                 if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
                 a.mapping_copy[t] = key - 1;
             }
