@@ -231,7 +231,8 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("prepare" if "prepare_kernel" in name else "shrink" if "shrink_kernel" in name else
+            key = ("prepare" if "prepare_kernel" in name else
+                   "shrink" if ("shrink_kernel" in name or "shrink_lds_kernel" in name) else
                    "expand" if "expand_kernel" in name else
                    ("preplinear" if "true>" in name.split(",")[-1] else "linear")
                    if ("fused_kernel" in name or "lora_major_kernel" in name) else
@@ -258,6 +259,46 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     with open(out_json, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+
+
+def summarize_mfma(workload: str, pmc_csv: str, out_md: str, command: str) -> None:
+    """MFMA use per lora kernel from one rocprofv3 --pmc run of
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA operations / 512),
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (both summed over the
+    device's instances; GRBM_GUI_ACTIVE over its 8 XCDs), next to the
+    algorithmic flops of the shrink (2*T*H*S*r) and expand (2*T*r*O, twice:
+    the buffer enters as bf16 hi and lo parts)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(pmc_csv)):
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        if name.startswith("lora::"):
+            vals[name[len("lora::"):]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    import workloads
+    wl = workloads.make_workload(workload)
+    ta = int((wl.mapping.numpy() >= 0).sum())
+    sp = wl.layers[0].spec
+    algo = {"shrink": 2.0 * ta * sp.hidden * len(sp.slices) * sp.rank,
+            "expand": 2.0 * 2 * ta * sp.rank * sum(sp.slices)}
+    lines = ["# MFMA use: %s workload" % workload, "", "Command:", "", "    " + command, "",
+             "| kernel | dispatches | MFMA bf16 GFLOP | algorithmic GFLOP | MFMA busy % of SIMD cycles |",
+             "|---|---|---|---|---|"]
+    for k, v in sorted(vals.items()):
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0])
+        gui = v.get("GRBM_GUI_ACTIVE", [1.0])
+        flops = 512.0 * sum(mops) / len(mops)
+        util = 100.0 * (sum(busy) / len(busy)) / ((sum(gui) / len(gui)) / 8.0 * 1024.0)
+        kind = "shrink" if "shrink" in k else "expand" if "expand" in k else None
+        lines.append("| %s | %d | %.3f | %s | %.1f |" % (k, len(mops), flops / 1e9,
+                     "%.3f" % (algo[kind] / 1e9) if kind else "-", util))
+    lines += ["", "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+              "the run is a short eager profile under the counter collector, so its cycle counts "
+              "include the collector's overhead."]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def load_traffic(workload: str, kernel: str):
@@ -290,9 +331,14 @@ def main():
                     help="run this many eager steps and a 256 MiB calibration copy, then exit (counter runs)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "COMMAND"),
                     help="write the per-kernel traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
+                    help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.workload, *args.summarize_mfma)
         return
 
     if args.gpus != 1:
