@@ -559,7 +559,12 @@ hipError_t launch_lora_major(const FusedArgs &fin, bool prepare, hipStream_t str
     const bool add = fin.e.add_inputs != 0;
     const LoraMajorFn fn = prepare ? pick<true>(mt, kse, add) : pick<false>(mt, kse, add);
     const size_t lds = sizeof(int) * (size_t)((prepare ? 2 : 1) * n);   // the id's tokens (, the key-0 tokens)
-    const long grid = (long)max_loras * (parts + f.blocks);
+    long expanders = f.blocks;   // one expand block per workgroup
+    if (const char *v = getenv("LORA_LM_EXPANDERS")) {   // tuning: expanders walking several blocks
+        const int want = atoi(v);
+        if (want > 0 && want < expanders) expanders = want;
+    }
+    const long grid = (long)max_loras * (parts + expanders);
     if (grid > resident_grid(reinterpret_cast<const void *>(fn), kThreads, lds)) return hipErrorNotSupported;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, stream, f);
     return hipGetLastError();
