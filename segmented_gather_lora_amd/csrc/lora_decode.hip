@@ -198,6 +198,11 @@ void lora_major_kernel(FusedArgs f) {
     int *const s_list = smem;         // this id's tokens
     int *const s_list0 = smem + n;    // key-0 tokens (metadata only)
 
+    // Weights, x and y are touched once per launch: their loads (and the y
+    // stores) are nontemporal, so the stream does not evict the ids, buffer
+    // rows and counters that the launch reuses (measured 14.1 -> 13.3 us on
+    // the decode shape).
+    //
     // the ids first: memory counters complete in order, so the token filter
     // then waits for them only, not for the weights issued after them.  A
     // prepared no-LoRA batch keeps the previous batch's id copy (prepare
@@ -236,8 +241,8 @@ void lora_major_kernel(FusedArgs f) {
                 const int o0 = kk + 8 <= kend ? kk : 0, o1 = kk + 16 <= kend ? kk + 8 : 0;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    av[s2][mt][0] = ld16(arow[mt] + o0);
-                    av[s2][mt][1] = ld16(arow[mt] + o1);
+                    av[s2][mt][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(arow[mt] + o0));
+                    av[s2][mt][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(arow[mt] + o1));
                 }
             }
         }
@@ -256,8 +261,8 @@ void lora_major_kernel(FusedArgs f) {
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int kk = kbeg + (wave + kWaves * s2) * 64 + g * 16;
                     const int o0 = kk + 8 <= kend ? kk : 0, o1 = kk + 16 <= kend ? kk + 8 : 0;
-                    xv[s2][0] = ld16(xrow + o0);
-                    xv[s2][1] = ld16(xrow + o1);
+                    xv[s2][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + o0));
+                    xv[s2][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xrow + o1));
                 }
                 // the part's flag after the first loads, which then do not wait for it
                 if (t == 0 && tid == 0)
@@ -354,7 +359,7 @@ void lora_major_kernel(FusedArgs f) {
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 const int kk = k * 32 + 8 * g;
-                w[qq][k] = ld16(row + (kk < rank ? kk : 0));
+                w[qq][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + (kk < rank ? kk : 0)));
             }
         }
         braw = bk.bptr ? *reinterpret_cast<const u32x2 *>(bk.bptr + (int64_t)L * bk.width + bk.grp)
@@ -372,7 +377,7 @@ void lora_major_kernel(FusedArgs f) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             ytok[r4] = token_at(t * kTile + 4 * g + r4);
-            yv[r4] = ADD ? *reinterpret_cast<const u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + bk.ycol)
+            yv[r4] = ADD ? __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + bk.ycol))
                          : u32x2{0u, 0u};
         }
     };
@@ -500,9 +505,9 @@ void lora_major_kernel(FusedArgs f) {
                 const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][r4] + bias1);
                 const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][r4] + bias2);
                 const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][r4] + bias3);
-                *reinterpret_cast<u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + bk.ycol) =
-                    u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
-                          pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
+                __builtin_nontemporal_store(u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                                                  pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))},
+                                            reinterpret_cast<u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + bk.ycol));
             }
         }
     }
