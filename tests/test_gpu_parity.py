@@ -597,6 +597,22 @@ def test_lora_major_shapes(case, prep, monkeypatch):
 
 
 @pytest.mark.parametrize("prep", [True, False])
+def test_lora_major_bad_ids_and_many_ids(prep, monkeypatch):
+    """The LoRA-major kernel (forced) on 200 ids with ids out of range mixed
+    in: prepare reports them and treats them as -1, and the kernel -- reading
+    the raw mapping with a prepare, the cleaned copy without -- leaves their
+    rows untouched."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
+    wl = workloads.random_case(721, 2000, 512, (64, 64), 16, 200, neg_fraction=0.1, bias=True)
+    m = wl.mapping.numpy().copy()
+    m[5::13] = 200
+    m[9::29] = -7
+    wl.mapping.copy_(torch.from_numpy(m))
+    print("lora-major bad ids", prep, flush=True)
+    H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=prep, fused=not prep)
+
+
+@pytest.mark.parametrize("prep", [True, False])
 @pytest.mark.parametrize("add_inputs", [True, False])
 def test_lora_major_skewed_batch(add_inputs, prep, monkeypatch):
     """One id holding 300 of 512 tokens (19 tiles for its part owners and
