@@ -77,16 +77,34 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     }
     __syncthreads();
 
+    // _reset values and the no-LoRA flag, then the pages' early return
+    // (sorted indices untouched; the mapping copy too unless it served as
+    // scratch for a long batch)
+    auto no_lora_exit = [&]() {
+        if (tid == 0) {
+            *a.no_lora = 1;
+            *a.status = s_bad ? LORA_ERR_ID_RANGE : 0;
+        }
+        for (int k = tid; k < nkeys; k += kThreads) {
+            a.active_ids[k] = -1;
+            a.counts[k] = 0;
+        }
+        for (int k = tid; k < nkeys + 1; k += kThreads) a.start_loc[k] = 0;
+    };
+
     // ---- 1. ranks within the wave's slice
     int packed[kSteps];
+    int ids[kSteps];
     bool any = false, bad = false;
-    for (int c0 = 0; c0 < steps; c0 += kSteps) {
-        int ids[kSteps];
+    auto load_chunk = [&](int c0) {
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) {   // one round trip for the chunk (addresses clamped)
             const int t = t0 + (c0 + q) * kWave + lane;
             ids[q] = a.mapping[t < n ? t : n - 1];
         }
+    };
+    for (int c0 = 0; c0 < steps; c0 += kSteps) {
+        load_chunk(c0);
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) {
             if (c0 + q >= steps) break;   // uniform
@@ -99,7 +117,10 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
             }
             const int key = id + 1;
             any |= valid && id != -1;
-            const uint64_t m = match_key(key, valid, nbits);
+            // a step whose valid tokens all share one key (an all -1 stretch, a
+            // run of one id) needs no per-bit ballots: they all match each other
+            const int k0 = __builtin_amdgcn_readfirstlane(key);
+            const uint64_t m = ballot(valid && key != k0) == 0 ? ballot(valid) : match_key(key, valid, nbits);
             const bool leader = valid && (m & lanemask_lt()) == 0;
             const int rank = s_cnt[wave][key] + __popcll(m & lanemask_lt());
             packed[q] = (key << kRankBits) | rank;
@@ -117,20 +138,13 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     if (ballot(bad) && lane == 0) atomicOr(&s_bad, 1);
     __syncthreads();
 
-    const bool no_lora = (s_any == 0);
-    if (tid == 0) {
-        *a.no_lora = no_lora ? 1 : 0;
-        *a.status = s_bad ? LORA_ERR_ID_RANGE : 0;
-    }
-    if (no_lora) {
-        // _reset values, then the pages' early return (sorted indices untouched;
-        // the mapping copy too unless it served as scratch for a long batch)
-        for (int k = tid; k < nkeys; k += kThreads) {
-            a.active_ids[k] = -1;
-            a.counts[k] = 0;
-        }
-        for (int k = tid; k < nkeys + 1; k += kThreads) a.start_loc[k] = 0;
+    if (s_any == 0) {
+        no_lora_exit();
         return;
+    }
+    if (tid == 0) {
+        *a.no_lora = 0;
+        *a.status = s_bad ? LORA_ERR_ID_RANGE : 0;
     }
 
     // ---- 2. histogram, scan over keys (nkeys <= kThreads: one key per thread), slice bases
