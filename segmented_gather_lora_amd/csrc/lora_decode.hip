@@ -21,11 +21,14 @@
 // and the reset by the last workgroup out are those of the tile-major kernel,
 // with the words of id L in place of those of tile L.
 //
-// The metadata arrays (LoRAKernelMeta.prepare_tensors on the
+// With the prepare in the launch (lora_prepare_shrink_expand) the ids are the
+// raw mapping, and the metadata arrays (LoRAKernelMeta.prepare_tensors on the
 // "lora_kernel_metadata" page), which nothing in this launch reads, are
 // written piecewise by the first expander of every id: its slot and its
 // stretch of the sorted indices, whose place follows from counting smaller
-// keys and present keys with ballots and a presence bitmap in LDS.
+// keys and present keys with ballots and a presence bitmap in LDS.  Without
+// it (lora_shrink_expand on a prepared batch) the ids are the prepared copy,
+// gated by the no-LoRA flag, and the metadata is left alone.
 //
 // Weights of an id the batch does not use are read for nothing, so the
 // launcher takes this kernel only for batches of at least 4 tokens per id
