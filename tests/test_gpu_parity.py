@@ -596,6 +596,19 @@ def test_lora_major_shapes(case, prep, monkeypatch):
     H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=prep, fused=not prep)
 
 
+@pytest.mark.parametrize("expanders", [1, 5])
+@pytest.mark.parametrize("prep", [True, False])
+def test_lora_major_expanders_walk_blocks(prep, expanders, monkeypatch):
+    """LoRA-major expanders that walk several 256-column blocks each (fewer
+    expander roles than blocks), on the decode shape and on two-tile ids."""
+    monkeypatch.setenv("LORA_FUSED_LAYOUT", "lora")
+    monkeypatch.setenv("LORA_LM_EXPANDERS", str(expanders))
+    for wl in (workloads.make_workload("decode"),
+               workloads.random_case(731, 1200, 1024, (512, 256), 16, 60, bias=True)):
+        print("lora-major walk", prep, expanders, wl.spec.name, flush=True)
+        H.run_and_check(wl, add_inputs=True, offset_start=8, ldy_extra=8, prep=prep, fused=not prep)
+
+
 @pytest.mark.parametrize("prep", [True, False])
 def test_lora_major_bad_ids_and_many_ids(prep, monkeypatch):
     """The LoRA-major kernel (forced) on 200 ids with ids out of range mixed
