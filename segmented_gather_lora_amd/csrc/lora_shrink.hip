@@ -458,11 +458,9 @@ const StagedCfg kStaged[] = {
     {2, 2, 2, 4, true, shrink_lds_kernel<2, 2, 2, 4>},      // 9: 32 x 32
     {4, 6, 2, 5, true, shrink_lds_kernel<4, 6, 2, 5>},      // 10: 64 x 96
     {8, 6, 2, 4, true, shrink_lds_kernel<8, 6, 2, 4>},      // 11: 128 x 96
-    {8, 6, 2, 5, false, shrink_lds_kernel<8, 6, 2, 5>},     // 12: 128 x 96, 5 stages
-    {8, 8, 4, 4, true, shrink_lds_kernel<8, 8, 4, 4>},      // 13: 128 x 128
-    {4, 12, 4, 4, false, shrink_lds_kernel<4, 12, 4, 4>},   // 14: 64 x 192, 4 stages
-    {8, 4, 4, 6, false, shrink_lds_kernel<8, 4, 4, 6>},     // 15: 128 x 64, 6 stages
-    {4, 6, 2, 7, false, shrink_lds_kernel<4, 6, 2, 7>},     // 16: 64 x 96, 7 stages
+    {8, 8, 4, 4, false, shrink_lds_kernel<8, 8, 4, 4>},     // 12: 128 x 128, 4 stages (one per CU)
+    {8, 8, 4, 2, true, shrink_lds_kernel<8, 8, 4, 2>},      // 13: 128 x 128, 2 stages (two per CU)
+    {4, 6, 2, 3, false, shrink_lds_kernel<4, 6, 2, 3>},     // 14: 64 x 96, 3 stages (two per CU)
 };
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 
