@@ -225,19 +225,33 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     import csv
     import collections
 
+    import workloads
+    specs = workloads.WORKLOADS[workload].layers
+    # layers issuing a kernel of each kind, in the order a step issues them
+    layers_of = {"shrink": [i for i, L in enumerate(specs) if not L.expand_only],
+                 "expand": list(range(len(specs))), "prepare": [0], "preplinear": [0], "copy": [0]}
+    # the default path's later layers call lora_shrink_expand
+    layers_of["linear"] = [i for i in layers_of["shrink"] if i > 0] or [0]
+
     def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        if rows and "Dispatch_Id" in rows[0]:
+            rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         vals = collections.defaultdict(list)
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
+        seen = collections.Counter()
+        for r in rows:
             name = r["Kernel_Name"]
-            key = ("prepare" if "prepare_kernel" in name else
-                   "shrink" if ("shrink_kernel" in name or "shrink_lds_kernel" in name) else
-                   "expand" if "expand_kernel" in name else
-                   ("preplinear" if "true>" in name.split(",")[-1] else "linear")
-                   if ("fused_kernel" in name or "lora_major_kernel" in name) else
-                   "copy" if ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()) else None)
-            if key:
+            kind = ("prepare" if "prepare_kernel" in name else
+                    "shrink" if ("shrink_kernel" in name or "shrink_lds_kernel" in name) else
+                    "expand" if "expand_kernel" in name else
+                    ("preplinear" if "true>" in name.split(",")[-1] else "linear")
+                    if ("fused_kernel" in name or "lora_major_kernel" in name) else
+                    "copy" if ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()) else None)
+            if kind:
+                lays = layers_of[kind]
+                li = lays[seen[kind] % len(lays)]   # the k-th dispatch of a kind belongs to layer k mod count
+                seen[kind] += 1
+                key = kind if kind in ("prepare", "copy") else "%s%d" % (kind, li)
                 vals[key].append(float(r["Counter_Value"]) * 1024.0)
         return vals
 
@@ -250,12 +264,12 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     wscale = copy_bytes / cw if cw else 1.0
     rec = {"workload": workload, "kernel_hash": kernel_source_hash(), "command": command,
            "copy_fetch_scale": fscale, "copy_write_scale": wscale, "traffic_bytes": {}, "raw": {}}
-    for k in ("prepare", "shrink", "expand", "linear", "preplinear"):
-        if f.get(k) and w.get(k):
+    for k in sorted(f):
+        if k != "copy" and w.get(k):
             fb = sum(f[k]) / len(f[k])
             wb = sum(w[k]) / len(w[k])
             rec["raw"][k] = {"fetch_bytes": fb, "write_bytes": wb, "dispatches": len(f[k])}
-            rec["traffic_bytes"][k + "0"] = round(fb * fscale + wb * wscale)
+            rec["traffic_bytes"][k] = round(fb * fscale + wb * wscale)
     with open(out_json, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
@@ -301,6 +315,39 @@ def summarize_mfma(workload: str, pmc_csv: str, out_md: str, command: str) -> No
     print("\n".join(lines))
 
 
+def one_launch(wl, li: int, with_prepare: bool) -> bool:
+    """Whether lora_shrink_expand (or lora_prepare_shrink_expand) runs layer
+    li in one launch: at most 24 * (1023 + 1) tokens (2048 with the prepare),
+    fewer than 24 tokens per LoRA id on average, S * r <= 64 and r <= 64, as
+    the library header states; otherwise the call makes the separate calls."""
+    n = wl.mapping.numel()
+    sp = wl.layers[li].spec
+    segs = min(n, wl.spec.max_loras + 1)
+    if n < 1 or n > 24 * 1024 or (with_prepare and n > 2048):
+        return False
+    return (n + segs - 1) // segs < 24 and len(sp.slices) * sp.rank <= 64 and sp.rank <= 64
+
+
+def summarize_stats(workload: str, stats_csv: str, out_md: str, command: str) -> None:
+    """Markdown table of a rocprofv3 --kernel-trace --stats summary
+    (kernel_stats.csv): calls and durations per kernel."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel statistics: %s workload" % workload, "", "Command:", "", "    " + command, "",
+             "kernel_hash: " + kernel_source_hash(), "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        name = name.split("(")[0] if "(" in name else name
+        lines.append("| %s | %s | %.3f | %.3f | %.3f | %.1f |" % (
+            name[:80], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def load_traffic(workload: str, kernel: str):
     path = os.path.join(ROOT, "profiles", "pmc_%s.json" % workload)
     if not os.path.exists(path):
@@ -331,11 +378,16 @@ def main():
                     help="run this many eager steps and a 256 MiB calibration copy, then exit (counter runs)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "COMMAND"),
                     help="write the per-kernel traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write the kernel statistics of one rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
                     help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.workload, *args.summarize_stats)
         return
     if args.summarize_mfma:
         summarize_mfma(args.workload, *args.summarize_mfma)
@@ -447,10 +499,22 @@ def main():
             used += ["shrink%d" % li, "expand%d" % li]
     if "preplinear0" not in used:
         used.insert(0, "prepare")
-    dom = max((k for k in used if k != "prepare"), key=lambda k: kern[k])
+    # A one-launch call outside its range runs as its separate kernels; the
+    # roofline is then taken on the slowest of those kernels, not on the call.
+    kernels = []
+    for k in used:
+        li = int(k[-1])
+        if k.startswith(("linear", "preplinear")) and not one_launch(wl, li, k.startswith("prep")):
+            kernels += ["shrink%d" % li, "expand%d" % li]
+        else:
+            kernels.append(k)
+    dom = max((k for k in kernels if k != "prepare"), key=lambda k: kern[k])
     achieved = bytes_of[dom] / (kern[dom] * 1e-3) / 1e9
     kname = {"shrink": "lora_shrink", "expand": "lora_expand", "linear": "lora_shrink_expand",
              "prepli": "lora_prepare_shrink_expand"}[dom[:6]]
+    if dom[:6] in ("shrink", "expand") and dom not in used:
+        kname += " (in %s)" % ("lora_prepare_shrink_expand" if "preplinear0" in used and dom.endswith("0")
+                               else "lora_shrink_expand")
     traffic = load_traffic(args.workload, dom)
     separate = [k for k in kern if k[:6] in ("shrink", "expand")]
     se_ms = sum(kern[k] for k in separate)
