@@ -338,8 +338,9 @@ def summarize_stats(workload: str, stats_csv: str, out_md: str, command: str) ->
              "kernel_hash: " + kernel_source_hash(), "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"].replace("|", "/")
-        name = name.split("(")[0] if "(" in name else name
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").replace("|", "/")
+        if name.endswith(")") and "(" in name:   # drop the parameter list
+            name = name[:name.rindex("(")]
         lines.append("| %s | %s | %.3f | %.3f | %.3f | %.1f |" % (
             name[:80], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             float(r["Percentage"])))
