@@ -504,9 +504,8 @@ def main():
     # roofline is then taken on the slowest of those kernels, not on the call.
     kernels = []
     for k in used:
-        li = int(k[-1])
-        if k.startswith(("linear", "preplinear")) and not one_launch(wl, li, k.startswith("prep")):
-            kernels += ["shrink%d" % li, "expand%d" % li]
+        if k.startswith(("linear", "preplinear")) and not one_launch(wl, int(k[-1]), k.startswith("prep")):
+            kernels += ["shrink%s" % k[-1], "expand%s" % k[-1]]
         else:
             kernels.append(k)
     dom = max((k for k in kernels if k != "prepare"), key=lambda k: kern[k])
