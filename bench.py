@@ -317,15 +317,14 @@ def summarize_mfma(workload: str, pmc_csv: str, out_md: str, command: str) -> No
 
 def one_launch(wl, li: int, with_prepare: bool) -> bool:
     """Whether lora_shrink_expand (or lora_prepare_shrink_expand) runs layer
-    li in one launch: at most 24 * (1023 + 1) tokens (2048 with the prepare),
-    fewer than 24 tokens per LoRA id on average, S * r <= 64 and r <= 64, as
-    the library header states; otherwise the call makes the separate calls."""
+    li in one launch; outside that range the call makes the separate calls.
+    The library answers (host only, no device work)."""
+    import segmented_gather_lora_amd as sgl
     n = wl.mapping.numel()
     sp = wl.layers[li].spec
-    segs = min(n, wl.spec.max_loras + 1)
-    if n < 1 or n > 24 * 1024 or (with_prepare and n > 2048):
+    if n < 1:
         return False
-    return (n + segs - 1) // segs < 24 and len(sp.slices) * sp.rank <= 64 and sp.rank <= 64
+    return sgl.lora_shrink_expand_launches(n, wl.spec.max_loras, len(sp.slices), sp.rank, with_prepare) == 1
 
 
 def summarize_stats(workload: str, stats_csv: str, out_md: str, command: str) -> None:

@@ -222,6 +222,21 @@ int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const voi
                                int64_t ldy, int offset_start, int add_inputs, lora_meta_t *meta, float scale,
                                hipStream_t stream);
 
+/*
+ * Kernel launches that lora_shrink_expand (with_prepare = 0) or
+ * lora_prepare_shrink_expand (with_prepare != 0) makes for a layer of a batch
+ * of num_tokens >= 1 tokens, rank `rank` and num_slices slices, with the
+ * metadata sized for max_loras: 1 when the call is one launch (the fused
+ * kernels' range: fewer than 24 tokens per LoRA id on average, num_slices *
+ * rank <= 64, rank <= 64, and with the prepare at most 2048 tokens), else the
+ * separate calls' count: 2 (shrink, expand) or 3 (prepare, shrink, expand).
+ * A batch whose every id is -1 still makes these launches (they touch
+ * nothing).  Host only: no device work, no HIP call.  Negative lora_status for
+ * arguments the calls themselves would reject.  A measurement aid: it tells
+ * which kernel durations make up a call.
+ */
+int lora_shrink_expand_launches(int num_tokens, int max_loras, int num_slices, int rank, int with_prepare);
+
 /* Static description of a status code. */
 const char *lora_status_string(int status);
 

@@ -40,7 +40,8 @@ LORA_MAX_SLICES = 8
 LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
-            "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_status_string")
+            "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_shrink_expand_launches",
+            "lora_status_string")
 
 
 class LoraError(RuntimeError):
@@ -90,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.lora_prepare_shrink_expand.restype = i32
     lib.lora_prepare_shrink_expand.argtypes = [P, i32, P, i64, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
                                                ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
+    lib.lora_shrink_expand_launches.restype = i32
+    lib.lora_shrink_expand_launches.argtypes = [i32, i32, i32, i32, i32]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [i32]
     return lib
@@ -115,6 +118,17 @@ def __getattr__(name):
 
 def lora_status_string(status: int) -> str:
     return _lib().lora_status_string(int(status)).decode()
+
+
+def lora_shrink_expand_launches(num_tokens: int, max_loras: int, num_slices: int, rank: int,
+                                with_prepare: bool) -> int:
+    """Kernel launches of lora_shrink_expand / lora_prepare_shrink_expand for
+    such a layer: 1 inside the one-launch range, else 2 or 3 (host only)."""
+    st = _lib().lora_shrink_expand_launches(int(num_tokens), int(max_loras), int(num_slices), int(rank),
+                                            1 if with_prepare else 0)
+    if st < 0:
+        raise LoraError(st, "lora_shrink_expand_launches")
+    return st
 
 
 def _check(st: int, where: str) -> None:

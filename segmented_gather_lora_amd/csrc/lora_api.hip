@@ -344,6 +344,17 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
     return LORA_OK;
 }
 
+int lora_shrink_expand_launches(int num_tokens, int max_loras, int num_slices, int rank, int with_prepare) {
+    if (num_tokens < 1 || num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
+    if (max_loras < 1 || max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
+    if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_SLICES;
+    if (rank < 8 || rank > LORA_MAX_RANK || rank % 8) return LORA_ERR_SHAPE;
+    if (env_int("LORA_FUSED") >= 0 &&
+        one_launch_range(num_tokens, (long)max_loras + 1, num_slices * rank, rank, with_prepare != 0))
+        return 1;
+    return with_prepare ? 3 : 2;
+}
+
 int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const void *x, int64_t ldx, int hidden,
                                const void *const *lora_a, const void *const *lora_b, const void *const *bias,
                                const int *slice_widths, int num_slices, int rank, float *buf, void *y,

@@ -54,7 +54,7 @@ __device__ __forceinline__ void reset_tile(int32_t *words, int parts) {
 }
 
 // Batches the one-launch kernels prepare themselves: at most this many tokens.
-constexpr int kPrepMaxTokens = 2048;
+constexpr int kPrepMaxTokens = (int)kPrepMaxTokensHost;
 
 }  // namespace
 

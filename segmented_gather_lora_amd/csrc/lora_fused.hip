@@ -589,8 +589,7 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
     const int n = sin.num_tokens;
     const int nslots = sin.meta.nslots;
     const int segs = nslots < n ? nslots : n;
-    if (!fused_batch(n, nslots) || sin.rows > 64 || sin.rank > 64) return hipErrorNotSupported;
-    if (prep && n > kPrepMaxTokens) return hipErrorNotSupported;
+    if (!one_launch_range(n, nslots, sin.rows, sin.rank, prep != nullptr)) return hipErrorNotSupported;
 
     FusedArgs f;
     memset(&f, 0, sizeof f);

@@ -420,4 +420,17 @@ inline bool fused_batch(long n, long nslots) {
     return (n + segs - 1) / segs < 24;
 }
 
+// Batches that a one-launch call prepares itself: at most this many tokens.
+constexpr long kPrepMaxTokensHost = 2048;
+
+// Whether lora_shrink_expand (with_prepare: lora_prepare_shrink_expand) runs
+// a layer of S * rank = rows weight rows in one launch: a decode-like batch
+// (fused_batch), rows <= 64 and rank <= 64, and with the prepare at most
+// kPrepMaxTokensHost tokens.  Host-only; the launcher and the launch-count
+// query both use it.
+inline bool one_launch_range(long n, long nslots, int rows, int rank, bool with_prepare) {
+    if (!fused_batch(n, nslots) || rows > 64 || rank > 64) return false;
+    return !with_prepare || n <= kPrepMaxTokensHost;
+}
+
 }  // namespace lora

@@ -4,6 +4,8 @@ import csv
 import json
 import types
 
+import pytest
+
 import bench
 
 
@@ -15,10 +17,25 @@ def _wl(n, max_loras, layers):
     return types.SimpleNamespace(mapping=mapping, spec=spec, layers=ls)
 
 
+def test_launch_count_query():
+    """The library's own answer (host only) at the edges of the one-launch range."""
+    import segmented_gather_lora_amd as sgl
+    q = sgl.lora_shrink_expand_launches
+    assert q(256, 32, 3, 16, True) == 1 and q(256, 32, 3, 16, False) == 1
+    assert q(2048, 1022, 3, 16, True) == 1 and q(2049, 1022, 3, 16, True) == 3
+    assert q(2049, 1022, 3, 16, False) == 1
+    assert q(23 * 33, 32, 3, 16, False) == 1 and q(23 * 33 + 1, 32, 3, 16, False) == 2
+    assert q(256, 32, 1, 64, False) == 1 and q(256, 32, 1, 72, False) == 2 and q(256, 32, 3, 32, False) == 2
+    assert q(23 * 1024, 1023, 1, 8, False) == 1 and q(23 * 1024 + 1, 1023, 1, 8, False) == 2
+    for bad in [(0, 32, 3, 16), (256, 0, 3, 16), (256, 32, 0, 16), (256, 32, 3, 12)]:
+        with pytest.raises(sgl.LoraError):
+            q(*bad, True)
+
+
 def test_one_launch_range():
     qkv16 = [((4096, 1024, 1024), 16)]
     assert bench.one_launch(_wl(256, 32, qkv16), 0, True)           # 256 / 33 ids: 8 per id
-    # at most 2048 tokens with the prepare, 24 * 1024 without
+    # at most 2048 tokens with the prepare
     assert bench.one_launch(_wl(2048, 1022, qkv16), 0, True)
     assert not bench.one_launch(_wl(2049, 1022, qkv16), 0, True)
     assert bench.one_launch(_wl(2049, 1022, qkv16), 0, False)

@@ -740,3 +740,63 @@ def test_prepare_fused_graph_replay():
         H.shrink_check(buf_g, buf_ref, bound)
         H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
     meta.struct.host_no_lora = None
+
+
+def _hip_runtime():
+    """The HIP runtime library torch has loaded (the same instance, not a second copy)."""
+    import ctypes
+    with open("/proc/self/maps") as fh:
+        paths = {ln.split()[-1] for ln in fh if "libamdhip64" in ln}
+    assert paths, "libamdhip64 is not loaded"
+    return ctypes.CDLL(sorted(paths)[0])
+
+
+def _kernel_nodes(graph) -> int:
+    import ctypes
+    hip = _hip_runtime()
+    g = ctypes.c_void_p(graph.raw_cuda_graph())
+    count = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(g, None, ctypes.byref(count)) == 0
+    nodes = (ctypes.c_void_p * count.value)()
+    assert hip.hipGraphGetNodes(g, nodes, ctypes.byref(count)) == 0
+    kinds = []
+    for i in range(count.value):
+        t = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0
+        kinds.append(t.value)
+    return sum(1 for k in kinds if k == 0)   # hipGraphNodeTypeKernel
+
+
+@pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("zipf", 1000), ("zipf", 3000),
+                                    ("prefill", 600), ("large", 300)])
+@pytest.mark.parametrize("prep", [True, False])
+def test_launch_count_query_matches_the_calls(name, n, prep):
+    """lora_shrink_expand_launches against the kernels a captured call really
+    launches: one inside the one-launch range, else the separate calls."""
+    sgl = H.lib()
+    wl = workloads.make_workload(name, num_tokens=n)
+    L = wl.layers[0]
+    D = H.DevLayer(L)
+    ntok = wl.mapping.numel()
+    mapping = wl.mapping.to("cuda")
+    meta = sgl.LoraMeta(wl.spec.max_loras, ntok)
+    buf = torch.zeros((len(L.spec.slices), ntok, L.spec.rank), dtype=torch.float32, device="cuda")
+    y = D.y0.clone()
+    sgl.lora_prepare_meta(mapping, meta)
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph(keep_graph=True)
+    except TypeError:
+        pytest.skip("this torch cannot keep the captured graph")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        if prep:
+            sgl.lora_prepare_shrink_expand(mapping, D.x, D.a, D.b, D.bias, buf, y, meta, L.spec.scale)
+        else:
+            sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, L.spec.scale)
+    torch.cuda.current_stream().wait_stream(s)
+    want = sgl.lora_shrink_expand_launches(ntok, wl.spec.max_loras, len(L.spec.slices), L.spec.rank, prep)
+    got = _kernel_nodes(g)
+    print("launches", name, n, prep, want, got, flush=True)
+    assert got == want
