@@ -47,7 +47,8 @@ def test_prepare_workload_mappings(name):
     (1, 1, 1, 0.0), (2, 63, 3, 0.3), (3, 64, 3, 0.3), (4, 65, 7, 0.3), (5, 1023, 32, 0.1),
     (6, 1024, 32, 0.0), (7, 1025, 128, 0.2), (8, 5000, 1023, 0.2), (9, 20000, 64, 0.05),
     (10, 3000, 1, 0.5), (11, 2049, 255, 0.0), (12, 777, 511, 0.9), (13, 70000, 1023, 0.1),
-    (14, 16384, 2, 0.0), (15, 16385, 1023, 0.5)])
+    (14, 16384, 2, 0.0), (15, 16385, 1023, 0.5),
+    (16, 2097152, 1023, 0.1), (17, 2097152, 2, 0.0)])   # the largest batch the library takes
 def test_prepare_random(seed, n, ml, neg):
     rng = np.random.default_rng(seed)
     m = rng.integers(0, ml, n).astype(np.int32)
@@ -146,6 +147,16 @@ def test_parity_full_size_sampled(name, sample):
     print("full size", name, flush=True)
     st = H.run_and_check(wl, add_inputs=True, sample=sample, seed=11)
     print(st, flush=True)
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_largest_batch_sampled(bias):
+    """The largest batch the library takes (2097152 tokens) over 1023 LoRAs:
+    metadata bit-exact, shrink and expand on a seeded sample of tokens that
+    covers the first and last token of segments."""
+    wl = workloads.random_case(500 + bias, 2097152, 64, (64, 16), 16, 1023, neg_fraction=0.1, bias=bias)
+    print("largest batch", bias, flush=True)
+    H.run_and_check(wl, add_inputs=True, sample=512, seed=3)
 
 
 def test_no_lora_full_size_touches_nothing():
