@@ -373,7 +373,6 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate through (0 = auto)")
-    ap.add_argument("--copy-probe", action="store_true", help="also run a plain 256 MiB device copy")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many eager steps and a 256 MiB calibration copy, then exit (counter runs)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "COMMAND"),
@@ -521,12 +520,22 @@ def main():
     calls_ms = sum(kern[k] for k in used)
     calls_bytes = sum(bytes_of[k] for k in used)
 
-    if args.copy_probe:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    # a plain 256 MiB device-to-device copy, timed with events on the current
+    # stream: the read + write bandwidth a simple streaming kernel reaches here
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    copies = 5
+    c0.record(st)
+    for _ in range(copies):
+        dst.copy_(src)
+    c1.record(st)
+    c1.synchronize()
+    copy_gbps = 2.0 * src.numel() * copies / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     spec = wl.spec
     layers_cfg = [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
@@ -560,7 +569,8 @@ def main():
                    "step": step_desc},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": bytes_of[dom], "avg_us": round(kern[dom] * 1e3, 3)},
+                     "algorithmic_bytes": bytes_of[dom], "avg_us": round(kern[dom] * 1e3, 3),
+                     "measured_copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4)},
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kern.items()},
         "step_calls": {"path": args.path, "us": round(calls_ms * 1e3, 3),
                         "tokens_per_s": round(n / (calls_ms * 1e-3), 1),
