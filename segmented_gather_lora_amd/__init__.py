@@ -143,6 +143,81 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _need(ok: bool, status: int, where: str, what: str) -> None:
+    if not ok:
+        raise LoraError(status, "%s: %s" % (where, what))
+
+
+def _dev(t, dtype, meta, where: str, name: str) -> None:
+    """A tensor the kernels read or write through a raw pointer: on meta's
+    device, of the element type the C ABI takes, rows of unit element stride.
+    What the C ABI cannot see is checked here, so that a host tensor or a
+    wrong element type raises instead of reaching a kernel."""
+    if not (t.is_cuda and t.device == meta.region.device):
+        raise TypeError("%s: %s must be on %s (got %s)" % (where, name, meta.region.device, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s: %s must be %s (got %s)" % (where, name, dtype, t.dtype))
+    _need(t.dim() == 0 or t.stride(-1) == 1 or t.numel() <= 1, LORA_ERR_SHAPE, where,
+          "%s needs unit stride in its last dimension" % name)
+
+
+def _weights(ts, meta, where: str, name: str, last: Optional[int], mid: Optional[Sequence] = None) -> None:
+    """Per-slice weight tensors [>= max_loras][rows][last], contiguous: every
+    id below max_loras indexes a whole matrix."""
+    import torch
+    for i, t in enumerate(ts):
+        _dev(t, torch.bfloat16, meta, where, "%s[%d]" % (name, i))
+        _need(t.dim() == 3 and t.is_contiguous(), LORA_ERR_SHAPE, where, "%s[%d] must be a contiguous 3-d tensor" % (name, i))
+        _need(t.shape[0] >= meta.max_loras, LORA_ERR_SHAPE, where,
+              "%s[%d] holds %d LoRAs, fewer than max_loras %d" % (name, i, t.shape[0], meta.max_loras))
+        if last is not None:
+            _need(t.shape[2] == last, LORA_ERR_SHAPE, where, "%s[%d] last dimension %d != %d" % (name, i, t.shape[2], last))
+        if mid is not None:
+            _need(t.shape[1] == mid[i], LORA_ERR_SHAPE, where, "%s[%d] rows %d != %d" % (name, i, t.shape[1], mid[i]))
+
+
+def _bias(bias, widths, meta, where: str) -> None:
+    import torch
+    if bias is None:
+        return
+    _need(len(bias) == len(widths), LORA_ERR_SLICES, where, "one bias entry per slice")
+    for i, t in enumerate(bias):
+        if t is None:
+            continue
+        _dev(t, torch.bfloat16, meta, where, "bias[%d]" % i)
+        _need(t.dim() == 2 and t.is_contiguous() and t.shape[0] >= meta.max_loras and t.shape[1] == widths[i],
+              LORA_ERR_SHAPE, where, "bias[%d] must be contiguous [>= max_loras][%d]" % (i, widths[i]))
+
+
+def _layer_checks(where: str, meta, n: int, x=None, lora_a=None, lora_b=None, bias=None, buf=None, y=None,
+                  offset_start: int = 0) -> None:
+    """The tensors of one layer call, checked before the library sees them.
+    The token count is checked against the batch first, with the status the
+    library gives it."""
+    import torch
+    _need(n == meta.num_tokens, LORA_ERR_NUM_TOKENS, where, "%d tokens, the batch has %d" % (n, meta.num_tokens))
+    rank = None
+    if buf is not None:
+        _dev(buf, torch.float32, meta, where, "buf")
+        _need(buf.dim() == 3 and buf.is_contiguous() and buf.shape[1] == n, LORA_ERR_SHAPE, where,
+              "buf must be contiguous [S][%d][r]" % n)
+        rank = buf.shape[2]
+    if x is not None:
+        _dev(x, torch.bfloat16, meta, where, "x")
+        _need(x.dim() == 2 and x.shape[0] == n, LORA_ERR_SHAPE, where, "x must be [%d][H]" % n)
+    if lora_a is not None:
+        _weights(lora_a, meta, where, "lora_a", x.shape[1] if x is not None else None,
+                 [rank] * len(lora_a) if rank is not None else None)
+    if lora_b is not None:
+        _weights(lora_b, meta, where, "lora_b", rank)
+        widths = [int(t.shape[1]) for t in lora_b]
+        _bias(bias, widths, meta, where)
+        if y is not None:
+            _dev(y, torch.bfloat16, meta, where, "y")
+            _need(y.dim() == 2 and y.shape[0] >= n and y.shape[1] >= offset_start + sum(widths), LORA_ERR_SHAPE,
+                  where, "y must be [>= %d][>= %d]" % (n, offset_start + sum(widths)))
+
+
 def _ptr_array(tensors) -> ctypes.Array:
     return (ctypes.c_void_p * len(tensors))(*[None if t is None else t.data_ptr() for t in tensors])
 
@@ -196,7 +271,11 @@ class LoraMeta:
 
 def lora_prepare_meta(mapping, meta: LoraMeta, stream=None) -> None:
     """mapping: int32 device tensor [N] of LoRA ids (-1 = none)."""
+    import torch
     n = mapping.numel()
+    if n:
+        _dev(mapping, torch.int32, meta, "lora_prepare_meta", "mapping")
+        _need(mapping.is_contiguous(), LORA_ERR_SHAPE, "lora_prepare_meta", "mapping must be contiguous")
     _check(_lib().lora_prepare_meta(mapping.data_ptr() if n else None, n, ctypes.byref(meta.struct),
                                  _stream(stream)), "lora_prepare_meta")
 
@@ -207,6 +286,8 @@ def lora_shrink(x, lora_a: Sequence, buf, meta: LoraMeta, scale: float, stream=N
     slice; buf fp32 [S][N][r] contiguous."""
     n, h = x.shape
     r = lora_a[0].shape[1]
+    _layer_checks("lora_shrink", meta, n, x=x, lora_a=lora_a, buf=buf)
+    _need(buf.shape[0] == len(lora_a) and buf.shape[2] == r, LORA_ERR_SHAPE, "lora_shrink", "buf must be [S][N][r]")
     ptrs = _ptr_array(lora_a)
     _check(_lib().lora_shrink(x.data_ptr(), x.stride(0), n, h, ptrs, len(lora_a), r, buf.data_ptr(),
                            ctypes.byref(meta.struct), float(scale), _stream(stream)), "lora_shrink")
@@ -218,6 +299,8 @@ def lora_expand(buf, lora_b: Sequence, bias: Optional[Sequence], y, meta: LoraMe
     buf fp32 [S][N][r]; lora_b bf16 [max_loras][O_i][r] per slice; bias None
     or per slice (None | bf16 [max_loras][O_i]); y bf16 [N][ldy]."""
     s, n, r = buf.shape
+    _layer_checks("lora_expand", meta, n, lora_b=lora_b, bias=bias, buf=buf, y=y, offset_start=offset_start)
+    _need(len(lora_b) == s, LORA_ERR_SLICES, "lora_expand", "one lora_b entry per buf slice")
     widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
     bptrs = _ptr_array(lora_b)
     biasptrs = None if bias is None else _ptr_array(bias)
@@ -233,6 +316,9 @@ def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Seq
     launch for decode-like batches).  Arguments as for the two calls."""
     n, h = x.shape
     s, _, r = buf.shape
+    _layer_checks("lora_shrink_expand", meta, n, x=x, lora_a=lora_a, lora_b=lora_b, bias=bias, buf=buf, y=y,
+                  offset_start=offset_start)
+    _need(len(lora_a) == s and len(lora_b) == s, LORA_ERR_SLICES, "lora_shrink_expand", "one weight per buf slice")
     widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
     biasptrs = None if bias is None else _ptr_array(bias)
     _check(_lib().lora_shrink_expand(x.data_ptr(), x.stride(0), n, h, _ptr_array(lora_a), _ptr_array(lora_b),
@@ -246,9 +332,23 @@ def lora_prepare_shrink_expand(mapping, x, lora_a: Sequence, lora_b: Sequence, b
                                stream=None) -> None:
     """lora_prepare_meta(mapping) then lora_shrink_expand, in one call (one
     launch for small decode-like batches)."""
+    import torch
     n = mapping.numel()
     _, h = x.shape
     s, _, r = buf.shape
+    where = "lora_prepare_shrink_expand"
+    if n:
+        _dev(mapping, torch.int32, meta, where, "mapping")
+        _need(mapping.is_contiguous(), LORA_ERR_SHAPE, where, "mapping must be contiguous")
+    _need(n <= meta.max_num_tokens, LORA_ERR_NUM_TOKENS, where, "more tokens than the metadata holds")
+    saved = meta.struct.num_tokens
+    meta.struct.num_tokens = n          # the layer is checked against the batch about to be prepared
+    try:
+        _layer_checks(where, meta, n, x=x, lora_a=lora_a, lora_b=lora_b, bias=bias, buf=buf, y=y,
+                      offset_start=offset_start)
+    finally:
+        meta.struct.num_tokens = saved
+    _need(len(lora_a) == s and len(lora_b) == s, LORA_ERR_SLICES, where, "one weight per buf slice")
     widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
     biasptrs = None if bias is None else _ptr_array(bias)
     _check(_lib().lora_prepare_shrink_expand(mapping.data_ptr() if n else None, n, x.data_ptr(), x.stride(0), h,

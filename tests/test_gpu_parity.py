@@ -326,6 +326,32 @@ def test_invalid_arguments_raise():
     assert e.value.status == sgl.LORA_ERR_SHAPE
     with pytest.raises(sgl.LoraError):
         sgl.lora_prepare_meta(torch.zeros(9, dtype=torch.int32, device="cuda"), meta)
+    # what the C ABI cannot see is refused by the binding before any launch
+    b = [torch.zeros((2, 32, 16), dtype=torch.bfloat16, device="cuda")]
+    y = torch.zeros((8, 32), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError):
+        sgl.lora_shrink(x.cpu(), a, buf, meta, 1.0)                           # a host tensor
+    with pytest.raises(TypeError):
+        sgl.lora_shrink(x.float(), a, buf, meta, 1.0)                         # wrong element type
+    with pytest.raises(TypeError):
+        sgl.lora_prepare_meta(torch.zeros(8, dtype=torch.int64, device="cuda"), meta)
+    with pytest.raises(sgl.LoraError) as e:                                   # 1 LoRA for max_loras 2
+        sgl.lora_shrink(x, [a[0][:1].contiguous()], buf, meta, 1.0)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    with pytest.raises(sgl.LoraError) as e:                                   # B of another rank
+        sgl.lora_expand(buf, [torch.zeros((2, 32, 8), dtype=torch.bfloat16, device="cuda")], None, y, meta)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    with pytest.raises(sgl.LoraError) as e:                                   # y with too few rows
+        sgl.lora_expand(buf, b, None, y[:5], meta)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    with pytest.raises(sgl.LoraError) as e:                                   # y narrower than the slices
+        sgl.lora_expand(buf, b, None, y, meta, offset_start=8)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    with pytest.raises(sgl.LoraError) as e:                                   # a transposed (strided) x
+        sgl.lora_shrink(torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda").t(), a, buf, meta, 1.0)
+    assert e.value.status == sgl.LORA_ERR_SHAPE
+    sgl.lora_expand(buf, b, None, y, meta)                                    # the valid call still runs
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("cfg", range(1, 16))
