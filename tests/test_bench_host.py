@@ -9,6 +9,13 @@ import pytest
 import bench
 
 
+@pytest.fixture(scope="module", autouse=True)
+def _library_built():
+    """The launch-count query is a host-only call into the library."""
+    from segmented_gather_lora_amd import _build
+    _build.ensure_built()
+
+
 def _wl(n, max_loras, layers):
     """A stand-in workload: n tokens, max_loras, and (slices, rank) per layer."""
     mapping = types.SimpleNamespace(numel=lambda: n)
