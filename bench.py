@@ -1,25 +1,36 @@
 """Benchmark of the segmented-gather multi-LoRA hot path on one MI355X.
 
-One step = one batch through the whole path: lora_prepare_meta, then per
-layer lora_shrink + lora_expand (add_inputs=1), on seeded synthetic inputs
-already resident in HBM.  Default workload: ``decode`` (N=256 tokens,
-H=4096, r=16, 32 LoRAs, q/k/v slices 4096/1024/1024, 10% of tokens -1).
+One step = one batch through the whole path on seeded synthetic inputs that
+are already resident in HBM: the batch's metadata (LoRAKernelMeta.prepare_tensors)
+and, per layer, PunicaWrapperGPU.add_lora_linear -- shrink into a fresh fp32
+buffer, then expand into y with add_inputs -- made as lora_prepare_shrink_expand
+for the first layer and lora_shrink_expand for the others (one launch for
+decode-like batches, the separate kernels otherwise).  Those calls write the
+buffer as a fresh one ("="), so a step needs no clearing pass.
+
+The headline line is the largest configuration, ``large`` (N=16384 tokens,
+H=8192, r=128, 128 LoRAs, q/k/v slices 8192/1024/1024), timed for exactly
+``--steps`` steps after ``--warmup`` untimed ones.  The same run adds one
+record per other workload (decode, prefill, Zipf per layer, the all -1 batch,
+logits, embedding), each timed over about ``--sub-ms`` milliseconds, and the
+practical ceilings of this part: a 256 MiB device copy, a streaming read of
+each workload's step bytes, and an empty launch.
 
 Cold caches: when one input set fits in the 256 MB last-level cache, the
 bench rotates through enough independent copies (>= 1 GiB in total) that
-every step reads data that is not cache resident.  Steps are replayed from a
-HIP graph (one graph holds one step per copy), as a serving loop replays its
-decode step; ``--eager`` launches every call from Python instead.
+every step reads data that is not cache resident.  Steps are replayed from HIP
+graphs (``--eager`` launches every call from Python instead).
 
 Prints ONE JSON line.  ``roofline`` refers to the kernel with the largest
-average duration; its duration is measured with HIP events on the stream the
-kernels run on, over graph replays of that kernel alone right after the
-timed region.  ``traffic`` comes from committed rocprofv3 PMC summaries
-(profiles/) when their kernel source hash matches the current sources.
+average duration in the timed step; durations are measured with HIP events on
+the stream the kernels run on, over graph replays of one call at a time.
+``traffic`` comes from committed rocprofv3 PMC summaries (profiles/) when
+their kernel source hash matches the current sources.
 """
 from __future__ import annotations
 
 import argparse
+import collections
 import hashlib
 import json
 import math
@@ -33,21 +44,31 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA shrink+expand tokens/sec at 1 GPU; achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
+HEADLINE = "large"
+SUBS = ("decode", "prefill", "zipf", "large_nolora", "logits", "embedding")
+PROBE_WG = 2048          # workgroups of the streaming-read probe
+EMPTY_WG = 1024          # workgroups of the empty-launch probe (the decode kernel's grid)
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Bytes the method must move per launch (inputs/outputs of active tokens
-    and active LoRAs only; each x row once, each active LoRA's weights once)."""
+    """Bytes the method must move per launch: inputs and outputs of active
+    tokens and active LoRAs only (each x row once, each active LoRA's weights
+    once per call).  The linear calls write the fp32 buffer once (a fresh
+    buffer) and the expand reads it once; lora_shrink on its own reads and
+    writes it ("+=").  The metadata: the mapping read, the id copy and the
+    sorted indices written (12 B per token)."""
     import numpy as np
     m = wl.mapping.numpy()
     n = m.size
     act = m[m >= 0]
     ta, la = int(act.size), int(np.unique(act).size)
-    out = {"prepare": 16 * n, "shrink": [], "expand": [], "T_a": ta, "L_a": la}
+    out = {"prepare": 12 * n, "shrink": [], "shrink_fresh": [], "expand": [], "T_a": ta, "L_a": la}
     for L in wl.layers:
         sp = L.spec
         S, r, H, O = len(sp.slices), sp.rank, sp.hidden, sum(sp.slices)
-        out["shrink"].append(0 if sp.expand_only else 2 * ta * H + 2 * la * S * r * H + 8 * S * ta * r)
+        base = 0 if sp.expand_only else 2 * ta * H + 2 * la * S * r * H
+        out["shrink"].append(0 if sp.expand_only else base + 8 * S * ta * r)
+        out["shrink_fresh"].append(0 if sp.expand_only else base + 4 * S * ta * r)
         bias = 2 * la * O if L.bias is not None else 0
         out["expand"].append(4 * S * ta * r + 2 * la * r * O + bias + 2 * ta * O * 2)
     return out
@@ -62,6 +83,39 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# ------------------------------------------------------------------ dispatch plan
+
+class Plan:
+    """The library calls a run makes, in order, with the kernel launches each
+    makes (from the library's own launch-count query): rocprofv3's kernel
+    trace is matched against it to give per-workload, per-layer durations."""
+
+    def __init__(self):
+        self.calls = []          # [workload, phase, tag, launches]
+        self.phase = "setup"
+        self.workload = ""
+
+    def add(self, tag: str, launches: int, times: int = 1):
+        if self.calls and self.calls[-1][:3] == [self.workload, self.phase, tag] and \
+                self.calls[-1][3] == launches:
+            self.calls[-1][4] += times
+        else:
+            self.calls.append([self.workload, self.phase, tag, launches, times])
+
+    def replay(self, seq, times: int):
+        """A captured sequence of (tag, launches) replayed `times` times."""
+        for _ in range(times):
+            for tag, k in seq:
+                self.add(tag, k)
+
+    def dump(self, path: str):
+        with open(path, "w") as fh:
+            json.dump({"calls": self.calls}, fh)
+
+
+PLAN = Plan()
+
+
 class DeviceSet:
     """One independent copy of the workload's inputs in HBM."""
 
@@ -69,6 +123,7 @@ class DeviceSet:
         import torch
         import segmented_gather_lora_amd as sgl
         n = wl.mapping.numel()
+        self.wl = wl
         self.n = n
         self.mapping = wl.mapping.to("cuda") if src is None else src.mapping.clone()
         self.meta = sgl.LoraMeta(wl.spec.max_loras, n)
@@ -93,30 +148,35 @@ class DeviceSet:
     def prepare(self):
         import segmented_gather_lora_amd as sgl
         sgl.lora_prepare_meta(self.mapping, self.meta)
+        PLAN.add("prepare", 1)
 
     def shrink(self, li):
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_shrink(d["x"], d["a"], d["buf"], self.meta, d["scale"])
+        PLAN.add("shrink%d" % li, 1)
 
     def expand(self, li):
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_expand(d["buf"], d["b"], d["bias"], d["y"], self.meta, offset_start=0, add_inputs=True)
+        PLAN.add("expand%d" % li, 1)
 
     def linear(self, li):
-        """shrink + expand of one layer in one lora_shrink_expand call."""
+        """add_lora_linear of one layer: one lora_shrink_expand call."""
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_shrink_expand(d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta, d["scale"],
                                offset_start=0, add_inputs=True)
+        PLAN.add("linear%d" % li, launches(self.wl, li, False))
 
     def prepare_linear(self, li):
-        """prepare + shrink + expand of one layer in one lora_prepare_shrink_expand call."""
+        """prepare + add_lora_linear of one layer: one lora_prepare_shrink_expand call."""
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_prepare_shrink_expand(self.mapping, d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta,
                                        d["scale"], offset_start=0, add_inputs=True)
+        PLAN.add("preplinear%d" % li, launches(self.wl, li, True))
 
     def step(self, path: str = "prepare_fused"):
         first = 0
@@ -131,8 +191,25 @@ class DeviceSet:
             elif path in ("fused", "prepare_fused"):
                 self.linear(li)
             else:
+                # the separate calls, with the fresh buffer cleared in the step
+                self.layers[li]["buf"].zero_()
                 self.shrink(li)
                 self.expand(li)
+
+
+def launches(wl, li: int, with_prepare: bool) -> int:
+    """Kernel launches of lora_shrink_expand (lora_prepare_shrink_expand) for
+    layer li: the library answers (host only, no device work)."""
+    import segmented_gather_lora_amd as sgl
+    n = wl.mapping.numel()
+    sp = wl.layers[li].spec
+    if n < 1:
+        return 0
+    return sgl.lora_shrink_expand_launches(n, wl.spec.max_loras, sp.hidden, len(sp.slices), sp.rank, with_prepare)
+
+
+def one_launch(wl, li: int, with_prepare: bool) -> bool:
+    return launches(wl, li, with_prepare) == 1
 
 
 def set_bytes(wl) -> int:
@@ -145,19 +222,24 @@ def set_bytes(wl) -> int:
     return tot
 
 
-def capture(fn, reps: int = 1):
+def capture(fn):
     import torch
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    saved = PLAN.phase
+    PLAN.phase = "capture"          # capture records launches; nothing runs
+    n0 = len(PLAN.calls)
     with torch.cuda.graph(g, stream=s):
-        for _ in range(reps):
-            fn()
+        fn()
+    seq = [(c[2], c[3]) for c in PLAN.calls[n0:] for _ in range(c[4])]
+    del PLAN.calls[n0:]
+    PLAN.phase = saved
     torch.cuda.current_stream().wait_stream(s)
-    return g
+    return g, seq
 
 
-def time_graph(g, replays: int) -> float:
+def time_graph(g, seq, replays: int) -> float:
     """Average ms per replay, HIP events on the replay stream."""
     import torch
     st = torch.cuda.current_stream()
@@ -167,71 +249,166 @@ def time_graph(g, replays: int) -> float:
         g.replay()
     e1.record(st)
     e1.synchronize()
+    PLAN.replay(seq, replays)
     return e0.elapsed_time(e1) / replays
 
 
+# ------------------------------------------------------------------ CPU baseline
+
 def cpu_baseline(wl, budget_s: float) -> dict:
-    """The oracle, as it is, on this host's cores: prepare + shrink + expand on
-    a bounded sample of the workload's tokens."""
+    """The oracle, as it is, on this host: prepare on the full mapping, then
+    shrink + expand of every layer on a bounded, seeded sample of the
+    workload's tokens; once on one thread and once on every core this process
+    may run on (len(os.sched_getaffinity(0)), stated)."""
     import numpy as np
     import oracle
     import workloads
     cores = len(os.sched_getaffinity(0))
-    cores = max(1, min(cores, 16))
     m = wl.mapping.numpy()
     n = m.size
+    bits = {}
+    for li, L in enumerate(wl.layers):
+        bits[li] = dict(x=None if L.spec.expand_only else workloads.bf16_bits(L.x),
+                        a=[workloads.bf16_bits(a) for a in L.lora_a], b=[workloads.bf16_bits(b) for b in L.lora_b],
+                        bias=None if L.bias is None else [workloads.bf16_bits(b) for b in L.bias],
+                        y=workloads.bf16_bits(L.y0))
 
-    def run(tokens):
+    def run(tokens, threads):
         oracle.prepare(m, wl.spec.max_loras)
-        for L in wl.layers:
-            sp = L.spec
+        for li, L in enumerate(wl.layers):
+            sp, bb = L.spec, bits[li]
             if sp.expand_only:
                 buf = np.ascontiguousarray(L.x.numpy()[:, tokens])
             else:
-                xb = workloads.bf16_bits(L.x)[tokens]
                 buf = np.zeros((len(sp.slices), tokens.size, sp.rank), np.float32)
-                oracle.shrink(xb, [workloads.bf16_bits(a) for a in L.lora_a], buf, m[tokens], sp.scale,
-                              wl.spec.max_loras, nthreads=cores)
-            y = np.ascontiguousarray(workloads.bf16_bits(L.y0)[tokens])
-            bias = None if L.bias is None else [workloads.bf16_bits(b) for b in L.bias]
-            oracle.expand(buf, [workloads.bf16_bits(b) for b in L.lora_b], bias, y, m[tokens],
-                          wl.spec.max_loras, add_inputs=True, nthreads=cores)
+                oracle.shrink(bb["x"][tokens], bb["a"], buf, m[tokens], sp.scale, wl.spec.max_loras, nthreads=threads)
+            y = np.ascontiguousarray(bb["y"][tokens])
+            oracle.expand(buf, bb["b"], bb["bias"], y, m[tokens], wl.spec.max_loras, add_inputs=True,
+                          nthreads=threads)
 
-    rng = np.random.default_rng(0)
-    probe = np.sort(rng.choice(n, size=min(n, 4 * cores), replace=False)).astype(np.int32)
-    t0 = time.perf_counter()
-    run(probe)
-    per_tok = (time.perf_counter() - t0) / probe.size
-    k = int(min(n, max(probe.size, budget_s / max(per_tok, 1e-9))))
-    tokens = np.sort(rng.choice(n, size=k, replace=False)).astype(np.int32)
-    reps, elapsed = 0, 0.0
-    t0 = time.perf_counter()
-    while True:
-        run(tokens)
-        reps += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s or reps >= 100000 or k < n:
-            break
-    sample = ("%d of %d tokens (seeded uniform sample), prepare on the full mapping, %d pass(es)"
-              % (k, n, reps)) if k < n else ("the full batch of %d tokens, %d pass(es)" % (n, reps))
-    return {"value": k * reps / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 2)}
+    def leg(threads, seed):
+        rng = np.random.default_rng(seed)
+        probe = np.sort(rng.choice(n, size=min(n, 2 * threads), replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        run(probe, threads)
+        per_tok = (time.perf_counter() - t0) / probe.size
+        k = int(min(n, max(probe.size, 0.8 * budget_s / max(per_tok, 1e-9))))
+        tokens = np.sort(rng.choice(n, size=k, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        run(tokens, threads)
+        el = time.perf_counter() - t0
+        return k, el
+
+    k1, e1 = leg(1, 0)
+    kn, en = leg(cores, 1)
+    return {"value": round(kn / en, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d tokens (seeded uniform sample) through shrink + expand of every layer, "
+                      "prepare on the full mapping; %d threads" % (kn, n, cores),
+            "seconds": round(en, 2),
+            "single_thread": {"value": round(k1 / e1, 1), "unit": "tokens/s", "cores": 1,
+                              "sample": "%d of %d tokens" % (k1, n), "seconds": round(e1, 2)}}
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+def _kind_of(name: str):
+    if "prepare_kernel" in name:
+        return "prepare"
+    if "zero_rows_kernel" in name:
+        return "zero"
+    if "shrink_kernel" in name or "shrink_lds_kernel" in name:
+        return "shrink"
+    if "expand_kernel" in name:
+        return "expand"
+    if "fused_kernel" in name or "lora_major_kernel" in name:
+        return "one_launch"
+    if "probe_read_kernel" in name:
+        return "probe_read"
+    if "probe_empty_kernel" in name:
+        return "probe_empty"
+    return None
+
+
+def _expected_kinds(tag: str, k: int):
+    """Kernel kinds a call of `tag` making k launches dispatches, in order."""
+    if tag.startswith(("linear", "preplinear")):
+        if k == 1:
+            return ["one_launch"]
+        kinds = ["prepare"] if tag.startswith("prep") else []
+        if k - len(kinds) == 3:
+            kinds.append("zero")
+        return kinds + ["shrink", "expand"]
+    for p in ("prepare", "shrink", "expand", "probe_read", "probe_empty"):
+        if tag.startswith(p):
+            return [p]
+    raise ValueError(tag)
+
+
+def summarize_trace(trace_csv: str, plan_json: str, out_md: str, command: str) -> dict:
+    """Per-workload, per-layer kernel durations from one rocprofv3
+    --kernel-trace run of bench.py --dispatch-plan: the library's dispatches,
+    in dispatch order, are matched one by one against the calls bench made."""
+    import csv
+    rows = [r for r in csv.DictReader(open(trace_csv)) if _kind_of(r["Kernel_Name"])]
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Start_Timestamp"
+    rows.sort(key=lambda r: int(r[key]))
+    plan = json.load(open(plan_json))["calls"]
+    expect = []
+    for wl, phase, tag, k, times in plan:
+        kinds = _expected_kinds(tag, k)
+        for _ in range(times):
+            for kind in kinds:
+                expect.append((wl, phase, tag, kind))
+    if len(expect) != len(rows):
+        raise SystemExit("trace has %d library dispatches, the plan %d" % (len(rows), len(expect)))
+    stats = collections.defaultdict(list)
+    names = {}
+    for (wl, phase, tag, kind), r in zip(expect, rows):
+        got = _kind_of(r["Kernel_Name"])
+        if got != kind:
+            raise SystemExit("dispatch %s: expected a %s kernel for %s/%s, trace has %s"
+                             % (r[key], kind, wl, tag, r["Kernel_Name"][:80]))
+        if phase not in ("timed", "per_call"):
+            continue
+        layer = "".join(ch for ch in tag if ch.isdigit())
+        label = kind if kind in ("prepare", "probe_read", "probe_empty") else "%s%s" % (kind, layer)
+        k2 = (wl, phase, tag, label)
+        stats[k2].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        names[k2] = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    lines = ["# rocprofv3 kernel trace by workload and layer", "", "Command:", "", "    " + command, "",
+             "kernel_hash: " + kernel_source_hash(), "",
+             "Library dispatches matched one by one, in dispatch order, with the calls bench.py made "
+             "(its --dispatch-plan).  `timed`: the timed steps; `per_call`: graphs of one call at a time, "
+             "whose HIP-event average is bench's `kernels_us`.", "",
+             "| workload | phase | call | kernel | dispatches | average us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
+    out = {}
+    for k2 in sorted(stats):
+        v = stats[k2]
+        avg = sum(v) / len(v) / 1e3
+        lines.append("| %s | %s | %s | %s %s | %d | %.3f | %.3f | %.3f |" % (
+            k2[0], k2[1], k2[2], k2[3], names[k2][:60], len(v), avg, min(v) / 1e3, max(v) / 1e3))
+        out["%s/%s/%s/%s" % k2] = round(avg, 3)
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return out
 
 
 def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, command: str) -> None:
     """Per-dispatch HBM traffic of each lora kernel from two rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), scaled by what the same
-    counters read for a plain 256 MiB device copy in the same run."""
+    runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) of bench.py
+    --profile-steps, scaled by what the same counters read for a plain
+    256 MiB device copy in the same run.  Dispatches are attributed to layers
+    in dispatch order: the k-th dispatch of a kind in a step belongs to the
+    k-th layer that issues that kind."""
     import csv
-    import collections
-
     import workloads
     specs = workloads.WORKLOADS[workload].layers
-    # layers issuing a kernel of each kind, in the order a step issues them
     layers_of = {"shrink": [i for i, L in enumerate(specs) if not L.expand_only],
                  "expand": list(range(len(specs))), "prepare": [0], "preplinear": [0], "copy": [0]}
-    # the default path's later layers call lora_shrink_expand
     layers_of["linear"] = [i for i in layers_of["shrink"] if i > 0] or [0]
+    layers_of["zero"] = layers_of["shrink"]
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -241,15 +418,14 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
         seen = collections.Counter()
         for r in rows:
             name = r["Kernel_Name"]
-            kind = ("prepare" if "prepare_kernel" in name else
-                    "shrink" if ("shrink_kernel" in name or "shrink_lds_kernel" in name) else
-                    "expand" if "expand_kernel" in name else
-                    ("preplinear" if "true>" in name.split(",")[-1] else "linear")
-                    if ("fused_kernel" in name or "lora_major_kernel" in name) else
-                    "copy" if ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()) else None)
-            if kind:
+            kind = _kind_of(name)
+            if kind == "one_launch":
+                kind = "preplinear" if "true>" in name.split(",")[-1] else "linear"
+            elif kind is None and ("copyBuffer" in name or "elementwise" in name or "copy" in name.lower()):
+                kind = "copy"
+            if kind in layers_of:
                 lays = layers_of[kind]
-                li = lays[seen[kind] % len(lays)]   # the k-th dispatch of a kind belongs to layer k mod count
+                li = lays[seen[kind] % len(lays)]
                 seen[kind] += 1
                 key = kind if kind in ("prepare", "copy") else "%s%d" % (kind, li)
                 vals[key].append(float(r["Counter_Value"]) * 1024.0)
@@ -257,7 +433,6 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
 
     f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     copy_bytes = float(256 << 20)
-    # the copy kernel is the largest-traffic dispatch of the copy kind
     cf = max(f["copy"]) if f.get("copy") else None
     cw = max(w["copy"]) if w.get("copy") else None
     fscale = copy_bytes / cf if cf else 1.0
@@ -276,14 +451,13 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
 
 
 def summarize_mfma(workload: str, pmc_csv: str, out_md: str, command: str) -> None:
-    """MFMA use per lora kernel from one rocprofv3 --pmc run of
+    """MFMA and VALU use per lora kernel from one rocprofv3 --pmc run of
     SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA operations / 512),
-    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (both summed over the
-    device's instances; GRBM_GUI_ACTIVE over its 8 XCDs), next to the
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU and GRBM_GUI_ACTIVE (summed over
+    the device's instances; GRBM_GUI_ACTIVE over its 8 XCDs), next to the
     algorithmic flops of the shrink (2*T*H*S*r) and expand (2*T*r*O, twice:
     the buffer enters as bf16 hi and lo parts)."""
     import csv
-    import collections
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(pmc_csv)):
         name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
@@ -295,54 +469,26 @@ def summarize_mfma(workload: str, pmc_csv: str, out_md: str, command: str) -> No
     sp = wl.layers[0].spec
     algo = {"shrink": 2.0 * ta * sp.hidden * len(sp.slices) * sp.rank,
             "expand": 2.0 * 2 * ta * sp.rank * sum(sp.slices)}
-    lines = ["# MFMA use: %s workload" % workload, "", "Command:", "", "    " + command, "",
-             "| kernel | dispatches | MFMA bf16 GFLOP | algorithmic GFLOP | MFMA busy % of SIMD cycles |",
-             "|---|---|---|---|---|"]
+    algo["one_launch"] = algo["shrink"] + algo["expand"]
+    lines = ["# MFMA and VALU use: %s workload" % workload, "", "Command:", "", "    " + command, "",
+             "kernel_hash: " + kernel_source_hash(), "",
+             "| kernel | dispatches | MFMA bf16 GFLOP | algorithmic GFLOP | MFMA busy % of SIMD cycles | "
+             "VALU instructions (M) |", "|---|---|---|---|---|---|"]
     for k, v in sorted(vals.items()):
-        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])
-        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0])
-        gui = v.get("GRBM_GUI_ACTIVE", [1.0])
-        flops = 512.0 * sum(mops) / len(mops)
-        util = 100.0 * (sum(busy) / len(busy)) / ((sum(gui) / len(gui)) / 8.0 * 1024.0)
-        kind = "shrink" if "shrink" in k else "expand" if "expand" in k else None
-        lines.append("| %s | %d | %.3f | %s | %.1f |" % (k, len(mops), flops / 1e9,
-                     "%.3f" % (algo[kind] / 1e9) if kind else "-", util))
+        def avg(c, d=0.0):
+            x = v.get(c, [d])
+            return sum(x) / len(x)
+        flops = 512.0 * avg("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        gui = avg("GRBM_GUI_ACTIVE", 1.0)
+        util = 100.0 * avg("SQ_VALU_MFMA_BUSY_CYCLES") / (gui / 8.0 * 1024.0)
+        kind = _kind_of(k)
+        lines.append("| %s | %d | %.3f | %s | %.1f | %s |" % (
+            k, len(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])), flops / 1e9,
+            "%.3f" % (algo[kind] / 1e9) if kind in algo else "-", util,
+            "%.2f" % (avg("SQ_INSTS_VALU") / 1e6) if "SQ_INSTS_VALU" in v else "-"))
     lines += ["", "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
               "the run is a short eager profile under the counter collector, so its cycle counts "
               "include the collector's overhead."]
-    with open(out_md, "w") as fh:
-        fh.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-def one_launch(wl, li: int, with_prepare: bool) -> bool:
-    """Whether lora_shrink_expand (or lora_prepare_shrink_expand) runs layer
-    li in one launch; outside that range the call makes the separate calls.
-    The library answers (host only, no device work)."""
-    import segmented_gather_lora_amd as sgl
-    n = wl.mapping.numel()
-    sp = wl.layers[li].spec
-    if n < 1:
-        return False
-    return sgl.lora_shrink_expand_launches(n, wl.spec.max_loras, len(sp.slices), sp.rank, with_prepare) == 1
-
-
-def summarize_stats(workload: str, stats_csv: str, out_md: str, command: str) -> None:
-    """Markdown table of a rocprofv3 --kernel-trace --stats summary
-    (kernel_stats.csv): calls and durations per kernel."""
-    import csv
-    rows = list(csv.DictReader(open(stats_csv)))
-    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = ["# rocprofv3 kernel statistics: %s workload" % workload, "", "Command:", "", "    " + command, "",
-             "kernel_hash: " + kernel_source_hash(), "",
-             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").replace("|", "/")
-        if name.endswith(")") and "(" in name:   # drop the parameter list
-            name = name[:name.rindex("(")]
-        lines.append("| %s | %s | %.3f | %.3f | %.3f | %.1f |" % (
-            name[:80], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            float(r["Percentage"])))
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -359,132 +505,175 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("traffic_bytes", {}).get(kernel)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode")
-    ap.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
-    ap.add_argument("--path", choices=("prepare_fused", "fused", "separate"), default="prepare_fused",
-                    help="prepare_fused: lora_prepare_shrink_expand for the first layer, lora_shrink_expand for "
-                         "the others; fused: lora_prepare_meta, then lora_shrink_expand per layer; separate: "
-                         "lora_prepare_meta, then lora_shrink and lora_expand per layer")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate through (0 = auto)")
-    ap.add_argument("--profile-steps", type=int, default=0,
-                    help="run this many eager steps and a 256 MiB calibration copy, then exit (counter runs)")
-    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "COMMAND"),
-                    help="write the per-kernel traffic summary of two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
-                    help="write the kernel statistics of one rocprofv3 --kernel-trace --stats run and exit")
-    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
-                    help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
-    args = ap.parse_args()
-    if args.summarize_pmc:
-        summarize_pmc(args.workload, *args.summarize_pmc)
-        return
-    if args.summarize_stats:
-        summarize_stats(args.workload, *args.summarize_stats)
-        return
-    if args.summarize_mfma:
-        summarize_mfma(args.workload, *args.summarize_mfma)
-        return
+# ------------------------------------------------------------------ measurement
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requested --gpus %d)." % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
+def copy_gbps() -> float:
+    """A plain 256 MiB device-to-device copy (read + write bytes per second)."""
     import torch
-    from segmented_gather_lora_amd import _build
-    _build.ensure_built()
-    import segmented_gather_lora_amd  # noqa: F401
-    import workloads
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(st)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(st)
+    c1.synchronize()
+    return 2.0 * src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
-    torch.cuda.set_device(0)
-    wl = workloads.make_workload(args.workload)
+
+def probe_read(nbytes: int, copies: int) -> dict:
+    """Streaming-read probe over `copies` rotated buffers of nbytes each (cold
+    reads when the set exceeds the last-level cache): average us per launch
+    and GB/s, replayed from a HIP graph like the step."""
+    import torch
+    import segmented_gather_lora_amd as sgl
+    nbytes = max(16, nbytes // 16 * 16)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(PROBE_WG, dtype=torch.float32, device="cuda")
+
+    def run():
+        for b in bufs:
+            sgl.lora_probe_read(b, PROBE_WG, sink)
+            PLAN.add("probe_read", 1)
+    run()
+    g, seq = capture(run)
+    g.replay()
+    PLAN.replay(seq, 1)
+    reps = max(2, int(math.ceil(50e-3 / max(1e-6, nbytes * copies / 5e12))))
+    ms = time_graph(g, seq, reps) / copies
+    del bufs
+    return {"us": round(ms * 1e3, 3), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
+            "workgroups": PROBE_WG}
+
+
+def probe_empty() -> float:
+    import segmented_gather_lora_amd as sgl
+
+    def run():
+        for _ in range(64):
+            sgl.lora_probe_empty(EMPTY_WG)
+            PLAN.add("probe_empty", 1)
+    run()
+    g, seq = capture(run)
+    g.replay()
+    PLAN.replay(seq, 1)
+    return time_graph(g, seq, 10) / 64 * 1e3
+
+
+def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float) -> dict:
+    """Time one workload: `steps` steps exactly (None: about sub_ms of steps),
+    then one call at a time for the per-kernel durations."""
+    import torch
+    import workloads
+    PLAN.workload = name
+    PLAN.phase = "setup"
+    wl = workloads.make_workload(name)
     n = wl.mapping.numel()
     ab = algorithmic_bytes(wl)
     sb = set_bytes(wl)
-    if args.rotate:
-        rotate = args.rotate
-    else:
-        rotate = max(1, math.ceil((1 << 30) / sb)) if sb < LLC_BYTES else 1
-    print("# workload %s: N=%d, %.1f MB per input set, rotating %d set(s)" % (args.workload, n, sb / 1e6, rotate),
+    rotate = args.rotate or (max(1, math.ceil((1 << 30) / sb)) if sb < LLC_BYTES else 1)
+    print("# %s: N=%d, %.1f MB per input set, rotating %d set(s)" % (name, n, sb / 1e6, rotate),
           file=sys.stderr, flush=True)
     first = DeviceSet(wl)
     sets = [first] + [DeviceSet(wl, src=first) for _ in range(rotate - 1)]
     nl = len(wl.layers)
-
-    # warm-up (eager; loads the code objects), then capture one step per set
     path = args.path
-    for i in range(max(args.warmup, rotate)):
+
+    PLAN.phase = "warmup"
+    for i in range(max(warmup, rotate)):
         sets[i % rotate].step(path)
     torch.cuda.synchronize()
 
     if args.profile_steps:
-        # short eager run for hardware-counter collection, plus a plain copy
-        # of known size that calibrates the byte counters
+        PLAN.phase = "profile"
         for i in range(args.profile_steps):
             sets[i % rotate].step(path)
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
-        print("# profile run done", file=sys.stderr)
-        return
+        return {}
 
-    steps = max(args.steps // rotate, 1) * rotate
+    # a graph holds per_graph steps cycling over the sets (at least 16 steps,
+    # a multiple of the rotation); a second graph holds the remainder, so the
+    # timed region is exactly `steps` steps
+    per_graph = rotate * max(1, math.ceil(16 / rotate))
     if args.eager:
+        steps = steps or 200
         torch.cuda.synchronize()
+        PLAN.phase = "timed"
         t0 = time.perf_counter()
         for i in range(steps):
             sets[i % rotate].step(path)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     else:
-        g = capture(lambda: [s.step(path) for s in sets])
-        for _ in range(max(1, args.warmup // rotate)):
-            g.replay()
+        g, seq = capture(lambda: [sets[i % rotate].step(path) for i in range(per_graph)])
+        PLAN.phase = "warmup"
+        g.replay()
+        PLAN.replay(seq, 1)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps // rotate):
+        if steps is None:   # about sub_ms of steps, in whole graphs
+            t0 = time.perf_counter()
             g.replay()
+            torch.cuda.synchronize()
+            PLAN.replay(seq, 1)
+            est = (time.perf_counter() - t0) / per_graph
+            steps = per_graph * max(1, int(math.ceil(sub_ms * 1e-3 / max(est, 1e-7) / per_graph)))
+        full, rem = divmod(steps, per_graph)
+        gr = sr = None
+        if rem:
+            gr, sr = capture(lambda: [sets[i % rotate].step(path) for i in range(rem)])
+            gr.replay()
+            PLAN.replay(sr, 1)
+        torch.cuda.synchronize()
+        PLAN.phase = "timed"
+        t0 = time.perf_counter()
+        for _ in range(full):
+            g.replay()
+        if gr is not None:
+            gr.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        PLAN.replay(seq, full)
+        if gr is not None:
+            PLAN.replay(sr, 1)
     ms_per_step = 1e3 * elapsed / steps
-    value = n * steps / elapsed
-    print("# timed %d steps in %.3f s" % (steps, elapsed), file=sys.stderr, flush=True)
+    print("# %s: timed %d steps in %.4f s" % (name, steps, elapsed), file=sys.stderr, flush=True)
 
-    # per-kernel average durations: graphs of >= 32 launches of one kernel kind
-    # cycling over the input sets (graph launch overhead amortised)
-    launches = max(32, rotate)
-    reps = max(2, 400 // launches)
+    # per-call average durations: graphs of >= 32 launches of one call kind
+    # cycling over the input sets
+    PLAN.phase = "per_call"
+    ncalls = max(32, rotate)
+    reps = 2
 
-    def per_launch(fn):
-        g1 = capture(lambda: [fn(sets[i % rotate]) for i in range(launches)])
+    def per_call(fn):
+        g1, s1 = capture(lambda: [fn(sets[i % rotate]) for i in range(ncalls)])
         g1.replay()
-        return time_graph(g1, reps) / launches
+        PLAN.replay(s1, 1)
+        return time_graph(g1, s1, reps) / ncalls
 
-    kern = {"prepare": per_launch(lambda s: s.prepare())}
+    kern = {}
+    if not all(L.spec.expand_only for L in wl.layers) or True:
+        kern["prepare"] = per_call(lambda s: s.prepare())
     for li in range(nl):
         if not wl.layers[li].spec.expand_only:
-            kern["shrink%d" % li] = per_launch(lambda s: s.shrink(li))
-            kern["linear%d" % li] = per_launch(lambda s: s.linear(li))
-        kern["expand%d" % li] = per_launch(lambda s: s.expand(li))
+            kern["shrink%d" % li] = per_call(lambda s: s.shrink(li))
+            kern["linear%d" % li] = per_call(lambda s: s.linear(li))
+        kern["expand%d" % li] = per_call(lambda s: s.expand(li))
     if not wl.layers[0].spec.expand_only:
-        kern["preplinear0"] = per_launch(lambda s: s.prepare_linear(0))
+        kern["preplinear0"] = per_call(lambda s: s.prepare_linear(0))
     torch.cuda.synchronize()
+
     bytes_of = {"prepare": ab["prepare"]}
     for li in range(nl):
         if not wl.layers[li].spec.expand_only:
             bytes_of["shrink%d" % li] = ab["shrink"][li]
-            bytes_of["linear%d" % li] = ab["shrink"][li] + ab["expand"][li]
+            bytes_of["shrink_fresh%d" % li] = ab["shrink_fresh"][li]
+            bytes_of["linear%d" % li] = ab["shrink_fresh"][li] + ab["expand"][li]
         bytes_of["expand%d" % li] = ab["expand"][li]
     if "preplinear0" in kern:
-        bytes_of["preplinear0"] = ab["prepare"] + ab["shrink"][0] + ab["expand"][0]
+        bytes_of["preplinear0"] = ab["prepare"] + ab["shrink_fresh"][0] + ab["expand"][0]
     # the calls the timed step makes
     used = []
     for li in range(nl):
@@ -498,49 +687,49 @@ def main():
             used += ["shrink%d" % li, "expand%d" % li]
     if "preplinear0" not in used:
         used.insert(0, "prepare")
-    # A one-launch call outside its range runs as its separate kernels; the
-    # roofline is then taken on the slowest of those kernels, not on the call.
+    # A one-launch call outside its range runs as its separate kernels: the
+    # roofline is then taken on the slowest of those kernels.
     kernels = []
     for k in used:
         if k.startswith(("linear", "preplinear")) and not one_launch(wl, int(k[-1]), k.startswith("prep")):
             kernels += ["shrink%s" % k[-1], "expand%s" % k[-1]]
         else:
             kernels.append(k)
-    dom = max((k for k in kernels if k != "prepare"), key=lambda k: kern[k])
-    achieved = bytes_of[dom] / (kern[dom] * 1e-3) / 1e9
-    kname = {"shrink": "lora_shrink", "expand": "lora_expand", "linear": "lora_shrink_expand",
-             "prepli": "lora_prepare_shrink_expand"}[dom[:6]]
-    if dom[:6] in ("shrink", "expand") and dom not in used:
-        kname += " (in %s)" % ("lora_prepare_shrink_expand" if "preplinear0" in used and dom.endswith("0")
-                               else "lora_shrink_expand")
-    traffic = load_traffic(args.workload, dom)
-    separate = [k for k in kern if k[:6] in ("shrink", "expand")]
-    se_ms = sum(kern[k] for k in separate)
-    se_bytes = sum(bytes_of[k] for k in separate)
-    calls_ms = sum(kern[k] for k in used)
-    calls_bytes = sum(bytes_of[k] for k in used)
-
-    # a plain 256 MiB device-to-device copy, timed with events on the current
-    # stream: the read + write bandwidth a simple streaming kernel reaches here
-    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    st = torch.cuda.current_stream()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    copies = 5
-    c0.record(st)
-    for _ in range(copies):
-        dst.copy_(src)
-    c1.record(st)
-    c1.synchronize()
-    copy_gbps = 2.0 * src.numel() * copies / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
-    spec = wl.spec
-    layers_cfg = [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
-                   "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
-                  for L in wl.layers]
+    step_bytes = sum(bytes_of[k] for k in used)
+    tokens_per_s = n / (ms_per_step * 1e-3)
+    rec = {"workload": name, "num_tokens": n, "max_loras": wl.spec.max_loras,
+           "active_tokens": ab["T_a"], "active_loras": ab["L_a"],
+           "layers": [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
+                       "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
+                      for L in wl.layers],
+           "input_sets_rotated": rotate, "steps": steps, "ms_per_step": round(ms_per_step, 5),
+           "tokens_per_s": round(tokens_per_s, 1), "step_bytes": step_bytes,
+           "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+           "step_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+    if ab["T_a"] == 0:
+        rec["roofline"] = None   # the all -1 batch moves no data: launch-latency bound
+    else:
+        # the shrink of a linear call writes a fresh buffer: its bytes use the
+        # write-only buffer term
+        def kbytes(k):
+            if k.startswith("shrink") and k not in used:
+                return bytes_of["shrink_fresh" + k[6:]]
+            return bytes_of[k]
+        dom = max((k for k in kernels if k != "prepare"), key=lambda k: kern[k])
+        achieved = kbytes(dom) / (kern[dom] * 1e-3) / 1e9
+        kname = {"shrink": "lora_shrink", "expand": "lora_expand", "linear": "lora_shrink_expand",
+                 "prepli": "lora_prepare_shrink_expand"}[dom[:6]]
+        if dom[:6] in ("shrink", "expand") and dom not in used:
+            kname += " (in %s)" % ("lora_prepare_shrink_expand" if "preplinear0" in used and dom.endswith("0")
+                                   else "lora_shrink_expand")
+        rec["roofline"] = {"bound": "hbm", "kernel": kname, "call": dom, "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": load_traffic(name, dom), "algorithmic_bytes": kbytes(dom),
+                           "avg_us": round(kern[dom] * 1e3, 3)}
+        # every kernel of the step against the peak
+        rec["kernel_frac"] = {k: round(kbytes(k) / (kern[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                              for k in kernels if k != "prepare"}
     parts = []
     for li, L in enumerate(wl.layers):
         if L.spec.expand_only:
@@ -548,40 +737,129 @@ def main():
         elif li == 0 and path == "prepare_fused":
             parts.append("prepare_shrink_expand")
         else:
-            parts.append("shrink_expand" if path != "separate" else "shrink + expand")
-    step_desc = ("" if "preplinear0" in used else "prepare + ") + " + ".join(parts)
+            parts.append("shrink_expand" if path != "separate" else "zero buf + shrink + expand")
+    rec["step"] = ("" if "preplinear0" in used else "prepare + ") + " + ".join(parts)
+    if not args.no_ceilings and ab["T_a"] > 0:
+        rec["read_probe"] = probe_read(step_bytes, rotate)
+        rec["frac_of_read_probe"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / rec["read_probe"]["GBps"], 4)
+    del sets, first
+    torch.cuda.empty_cache()
+    rec["_wl"] = wl
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50, help="headline steps timed, exactly")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, help="the headline workload")
+    ap.add_argument("--sub", default=",".join(SUBS),
+                    help="comma-separated workloads reported next to the headline ('none': no others)")
+    ap.add_argument("--sub-ms", type=float, default=100.0, help="timed milliseconds per other workload")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
+    ap.add_argument("--path", choices=("prepare_fused", "fused", "separate"), default="prepare_fused",
+                    help="prepare_fused: lora_prepare_shrink_expand for the first layer, lora_shrink_expand for "
+                         "the others; fused: lora_prepare_meta, then lora_shrink_expand per layer; separate: "
+                         "lora_prepare_meta, then per layer a cleared buffer, lora_shrink and lora_expand")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds per oracle leg (1 thread, all cores)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the read, copy and empty-launch probes")
+    ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate through (0 = auto)")
+    ap.add_argument("--dispatch-plan", default="", help="write the library calls made, in order, to this JSON")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many eager steps of --workload and a 256 MiB calibration copy, then exit "
+                         "(counter runs)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "COMMAND"),
+                    help="write the per-kernel traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_CSV", "PLAN_JSON", "OUT_MD", "COMMAND"),
+                    help="write per-workload, per-layer kernel durations of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
+                    help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.workload, *args.summarize_mfma)
+        return
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the segmented-gather LoRA path here has no multi-GPU part "
+              "(requested --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from segmented_gather_lora_amd import _build
+    _build.ensure_built()
+    import segmented_gather_lora_amd  # noqa: F401
+
+    torch.cuda.set_device(0)
+    if args.profile_steps:
+        run_workload(args.workload, args, None, args.warmup, 0)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("# profile run done", file=sys.stderr)
+        return
+
+    head = run_workload(args.workload, args, args.steps, args.warmup, 0)
+    wl = head.pop("_wl")
+    subs = {}
+    names = [] if args.sub in ("", "none") else [s for s in args.sub.split(",") if s and s != args.workload]
+    for s in names:
+        r = run_workload(s, args, None, min(args.warmup, 10), args.sub_ms)
+        r.pop("_wl")
+        subs[s] = r
+    ceil = {}
+    if not args.no_ceilings:
+        PLAN.workload, PLAN.phase = "probes", "per_call"
+        ceil = {"copy_256MiB_GBps": round(copy_gbps(), 1), "empty_launch_us": round(probe_empty(), 3),
+                "empty_launch_workgroups": EMPTY_WG}
+
+    roof = dict(head["roofline"])
+    if ceil:
+        roof["measured_copy_GBps"] = ceil["copy_256MiB_GBps"]
+        roof["frac_of_copy"] = round(roof["achieved"] / ceil["copy_256MiB_GBps"], 4)
+    if "read_probe" in head:
+        roof["measured_read_GBps"] = head["read_probe"]["GBps"]
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "num_tokens": n, "max_loras": spec.max_loras, "layers": layers_cfg,
-                   "active_tokens": ab["T_a"], "active_loras": ab["L_a"], "parallelism": "none",
-                   "launch": "eager" if args.eager else "hip_graph", "input_sets_rotated": rotate,
-                   "step": step_desc},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": bytes_of[dom], "avg_us": round(kern[dom] * 1e3, 3),
-                     "measured_copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4)},
-        "kernels_us": {k: round(v * 1e3, 3) for k, v in kern.items()},
-        "step_calls": {"path": args.path, "us": round(calls_ms * 1e3, 3),
-                        "tokens_per_s": round(n / (calls_ms * 1e-3), 1),
-                        "GBps": round(calls_bytes / (calls_ms * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(calls_bytes / (calls_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "shrink_expand": {"us": round(se_ms * 1e3, 3), "tokens_per_s": round(n / (se_ms * 1e-3), 1),
-                          "GBps": round(se_bytes / (se_ms * 1e-3) / 1e9, 1),
-                          "frac_of_peak": round(se_bytes / (se_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "config": {"workload": head["workload"], "num_tokens": head["num_tokens"], "max_loras": head["max_loras"],
+                   "layers": head["layers"], "active_tokens": head["active_tokens"],
+                   "active_loras": head["active_loras"], "parallelism": "none",
+                   "launch": "eager" if args.eager else "hip_graph", "input_sets_rotated": head["input_sets_rotated"],
+                   "step": head["step"], "path": args.path},
+        "roofline": roof,
+        "step_GBps": head["step_GBps"],
+        "step_frac_of_peak": head["step_frac_of_peak"],
+        "kernels_us": head["kernels_us"],
+        "kernel_frac": head.get("kernel_frac"),
+        "workloads": subs,
+        "ceilings": ceil,
     }
+    if "read_probe" in head:
+        line["ceilings"]["read_probe_" + head["workload"]] = head["read_probe"]
+        line["frac_of_read_probe"] = head["frac_of_read_probe"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    if args.dispatch_plan:
+        PLAN.dump(args.dispatch_plan)
     print(json.dumps(line), flush=True)
 
 

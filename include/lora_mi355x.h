@@ -67,9 +67,11 @@ typedef enum lora_status {
  *   no_lora_flag           int32[1]   1 when every id is -1 (or N == 0)
  *   status                 int32[1]   0, or LORA_ERR_ID_RANGE when some id was
  *                                     outside [-1, max_loras) (such ids count as -1)
- *   sync                   int32[128 * (ceil(min(max_num_tokens, 24576) / 16)
- *                                + min(max_loras + 1, max_num_tokens) + 1)]
- *                                     counters of lora_shrink_expand
+ *   sync                   int32[128 * (ceil(T / 16) + min(max_loras + 1, T) + 1)]
+ *                          followed by float32[64 * T] and float32[1024 * min(T, 2048)],
+ *                          T = min(max_num_tokens, 24576): counters, accumulation
+ *                                     area and part slots of the one-launch calls
+ *                                     (library-owned)
  * The struct itself lives in host memory; lora_prepare_meta() records
  * num_tokens in it.
  */
@@ -81,9 +83,12 @@ typedef struct lora_meta {
     int32_t *lora_token_start_loc;
     int32_t *no_lora_flag;
     int32_t *status;
-    int32_t *sync;           /* work counters of lora_shrink_expand (library-owned part of
-                                the region): zeroed by lora_prepare_meta, left zero by
-                                every lora_shrink_expand */
+    int32_t *sync;           /* work counters, fp32 accumulation area and part slots of the
+                                one-launch calls (library-owned part of the region): the
+                                counters and the accumulation area are zeroed by
+                                lora_prepare_meta for batches those calls can take and left
+                                zero by every such call that completes without
+                                LORA_ERR_SYNC; the part slots need no clearing */
     int32_t *host_no_lora;   /* optional host pinned word (NULL = none): prepare copies
                                 no_lora_flag into it asynchronously on its stream */
     int32_t max_loras;
@@ -168,28 +173,41 @@ int lora_expand(const float *buf, int num_tokens, int rank,
                 const lora_meta_t *meta, hipStream_t stream);
 
 /*
- * lora_shrink followed by lora_expand on the same buffer, as
- * PunicaWrapperGPU.add_lora_linear on the "punica_gpu" page chains them
- * (add_shrink into the fp32 buffer, then add_expand of that buffer), in one
- * call: the arguments, layouts and results are exactly those of
- *     lora_shrink(x, ldx, N, hidden, lora_a, S, rank, buf, meta, scale, stream);
- *     lora_expand(buf, N, rank, lora_b, bias, slice_widths, S, y, ldy,
- *                 offset_start, add_inputs, meta, stream);
- * buf ends holding the shrink result (buf += scale * x A^T) and y the expand
- * result.  For batches of short segments (decode-like: expected tokens per
- * LoRA below 24, S * rank <= 64, rank <= 64) both steps run in one launch:
- * the workgroups of each 16-token tile run its shrink parts, then wait on the
- * device until every part is done before their share of the tile's expand
+ * PunicaWrapperGPU.add_lora_linear on the "punica_gpu" page in one call: that
+ * method allocates a zeroed fp32 buffer, runs add_shrink into it and then
+ * add_expand from it.  Here `buf` is that buffer, supplied by the caller:
+ *     buf[i][t][j] = scale * sum_k x[t][k] * lora_a[i][m][j][k]    (j < rank)
+ *     then y as lora_expand(buf, ...) computes it,
+ * for every token t whose id m is not -1.  buf's contents on entry are
+ * ignored ("=" where lora_shrink has "+=": the same result on the freshly
+ * zeroed buffer of add_lora_linear, so the caller needs no clearing pass);
+ * rows of tokens with id -1 are not touched, and with the no-LoRA flag set
+ * nothing is.  Arguments, layouts and errors are those of lora_shrink and
+ * lora_expand.
+ * For batches of short segments (decode-like: expected tokens per LoRA below
+ * 24, S * rank <= 64, rank <= 64) both steps run in one launch: workgroups
+ * run K chunks ("parts") of a tile's shrink, adding their partial sums with
+ * float atomics into the accumulation area of meta->sync, count each part
+ * done, and the tile's expand waits on the device until every part is done
  * (a waiter that sees no progress runs the parts nobody has started, so the
- * wait needs no co-residency).  With at least 4 tokens per LoRA id (and every
- * role resident at once) the launch is laid out by LoRA id instead, reading
- * the prepared id copy (token_lora_mapping) rather than the sorted indices.
- * Other shapes launch the two kernels.  The fused
- * launch uses meta->sync; calls sharing one metadata region must not overlap
- * (they are ordered on one stream in normal use), and meta must have been
- * prepared at least once since it was bound.  Errors are those of the two
- * calls; a device-side wait that never ends (not expected) gives up after
- * about 0.1 s and sets meta->status to LORA_ERR_SYNC.
+ * wait needs no co-residency).  With at least 4 tokens per LoRA id, at most
+ * 2048 tokens, at most 16 parts of 512 (hidden <= 8192) and every role
+ * resident at once, the launch is laid out by LoRA id instead, reading the
+ * prepared id copy (token_lora_mapping) rather than the sorted indices; its
+ * parts store their sums in part slots of meta->sync and the expand adds them
+ * up in part order, so buf is deterministic in that layout.
+ * Other shapes launch the separate kernels (a split-K shrink also zeroes the
+ * active rows of buf first).  The one-launch kernels use meta->sync: calls
+ * sharing one metadata region must not overlap (they are ordered on one
+ * stream in normal use), and meta must have been prepared at least once since
+ * it was bound; every call that completes normally leaves the counters and
+ * the accumulation area zero.
+ * A device-side wait that never ends (not expected: every wait is on a
+ * running workgroup) gives up after about 0.1 s and sets meta->status to
+ * LORA_ERR_SYNC.  After that, y, buf and the counters and accumulation area
+ * of meta->sync are unspecified: the call's results must be discarded, and
+ * a lora_prepare_meta of a batch the one-launch calls can take must run
+ * before the next one-launch call (it clears the counters and the area).
  */
 int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
                        const void *const *lora_a, const void *const *lora_b, const void *const *bias,
@@ -209,10 +227,13 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
  * segment) and the metadata arrays are written piecewise by each id's first
  * expander.  Otherwise every workgroup sorts the mapping in its own LDS (the
  * same stable counting sort as lora_prepare_meta) and workgroup 0 writes the
- * metadata arrays.  Outside the range the two calls are made.  As for
- * lora_shrink_expand, the counters in meta->sync must start at zero: meta
- * must have been prepared since it was bound with at least as many tokens
- * (or its region zeroed once when allocated); every call leaves them zero.
+ * metadata arrays.  Outside the range the two calls are made.  buf is
+ * written as by lora_shrink_expand ("=", a fresh buffer).  As for
+ * lora_shrink_expand, the counters and the accumulation area in meta->sync
+ * must start at zero: meta must have been prepared since it was bound with at
+ * least as many tokens (or its region zeroed once when allocated); every call
+ * leaves them zero.  LORA_ERR_SYNC in meta->status leaves y, buf, the
+ * metadata arrays and meta->sync unspecified, as for lora_shrink_expand.
  * Records meta->num_tokens and copies the no-LoRA flag to meta->host_no_lora
  * when that is set.
  */
@@ -225,20 +246,38 @@ int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const voi
 /*
  * Kernel launches that lora_shrink_expand (with_prepare = 0) or
  * lora_prepare_shrink_expand (with_prepare != 0) makes for a layer of a batch
- * of num_tokens >= 1 tokens, rank `rank` and num_slices slices, with the
- * metadata sized for max_loras: 1 when the call is one launch (the fused
- * kernels' range: fewer than 24 tokens per LoRA id on average, num_slices *
- * rank <= 64, rank <= 64, and with the prepare at most 2048 tokens), else the
- * separate calls' count: 2 (shrink, expand) or 3 (prepare, shrink, expand).
- * A batch whose every id is -1 still makes these launches (they touch
- * nothing).  Host only: no device work, no HIP call.  Negative lora_status for
- * arguments the calls themselves would reject.  A measurement aid: it tells
- * which kernel durations make up a call.
+ * of num_tokens >= 1 tokens, input width `hidden`, rank `rank` and
+ * num_slices slices, with the metadata sized for max_loras: 1 when the call is
+ * one launch (the fused kernels' range: fewer than 24 tokens per LoRA id on
+ * average, num_slices * rank <= 64, rank <= 64, and with the prepare at most
+ * 2048 tokens), else the separate calls' count: prepare (with_prepare), the
+ * zeroing of buf's active rows when the shrink is split over K chunks, shrink
+ * and expand.  A batch whose every id is -1 still makes these launches (they
+ * touch nothing).  Host only: no device work, no HIP call.  Negative
+ * lora_status for arguments the calls themselves would reject.  A measurement
+ * aid: it tells which kernel durations make up a call.
  */
-int lora_shrink_expand_launches(int num_tokens, int max_loras, int num_slices, int rank, int with_prepare);
+int lora_shrink_expand_launches(int num_tokens, int max_loras, int hidden, int num_slices, int rank,
+                                int with_prepare);
 
 /* Static description of a status code. */
 const char *lora_status_string(int status);
+
+/*
+ * Measurement aids (not part of the method; bench.py times them next to the
+ * calls above as practical ceilings).
+ *
+ * lora_probe_read: one launch of `workgroups` workgroups of 256 threads that
+ * reads `bytes` (> 0, a multiple of 16) of device memory at `src` (16-byte
+ * aligned) once, with streaming 16-byte loads, each workgroup a contiguous
+ * share.  `sink` is a device float[workgroups] the kernel may write (it never
+ * does for data whose 16-byte words do not fold to one particular pattern).
+ * lora_probe_empty: one launch of `workgroups` workgroups of 256 threads that
+ * do nothing.  Both are asynchronous on `stream`; LORA_ERR_NULL /
+ * LORA_ERR_SHAPE / LORA_ERR_ALIGN for bad arguments, checked on the host.
+ */
+int lora_probe_read(const void *src, size_t bytes, int workgroups, float *sink, hipStream_t stream);
+int lora_probe_empty(int workgroups, hipStream_t stream);
 
 #ifdef __cplusplus
 }

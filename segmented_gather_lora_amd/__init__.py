@@ -5,7 +5,9 @@ Torch tensors supply device memory and the current HIP stream.  The names
 mirror the C ABI in include/lora_mi355x.h:
 
     lora_meta_bytes, lora_meta_bind, lora_prepare_meta, lora_shrink,
-    lora_expand, lora_shrink_expand, lora_prepare_shrink_expand, lora_status_string
+    lora_expand, lora_shrink_expand, lora_prepare_shrink_expand,
+    lora_shrink_expand_launches, lora_status_string, and the measurement aids
+    lora_probe_read, lora_probe_empty
 
 plus ``LoraMeta``, a holder that owns one device region sized by
 ``lora_meta_bytes`` (LoRAKernelMeta.make on the "lora_kernel_metadata" page)
@@ -41,7 +43,7 @@ LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
             "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_shrink_expand_launches",
-            "lora_status_string")
+            "lora_status_string", "lora_probe_read", "lora_probe_empty")
 
 
 class LoraError(RuntimeError):
@@ -92,9 +94,13 @@ def _load() -> ctypes.CDLL:
     lib.lora_prepare_shrink_expand.argtypes = [P, i32, P, i64, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
                                                ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
     lib.lora_shrink_expand_launches.restype = i32
-    lib.lora_shrink_expand_launches.argtypes = [i32, i32, i32, i32, i32]
+    lib.lora_shrink_expand_launches.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [i32]
+    lib.lora_probe_read.restype = i32
+    lib.lora_probe_read.argtypes = [P, ctypes.c_size_t, i32, P, P]
+    lib.lora_probe_empty.restype = i32
+    lib.lora_probe_empty.argtypes = [i32, P]
     return lib
 
 
@@ -120,15 +126,33 @@ def lora_status_string(status: int) -> str:
     return _lib().lora_status_string(int(status)).decode()
 
 
-def lora_shrink_expand_launches(num_tokens: int, max_loras: int, num_slices: int, rank: int,
+def lora_shrink_expand_launches(num_tokens: int, max_loras: int, hidden: int, num_slices: int, rank: int,
                                 with_prepare: bool) -> int:
     """Kernel launches of lora_shrink_expand / lora_prepare_shrink_expand for
-    such a layer: 1 inside the one-launch range, else 2 or 3 (host only)."""
-    st = _lib().lora_shrink_expand_launches(int(num_tokens), int(max_loras), int(num_slices), int(rank),
-                                            1 if with_prepare else 0)
+    such a layer: 1 inside the one-launch range, else the separate calls'
+    count (host only)."""
+    st = _lib().lora_shrink_expand_launches(int(num_tokens), int(max_loras), int(hidden), int(num_slices),
+                                            int(rank), 1 if with_prepare else 0)
     if st < 0:
         raise LoraError(st, "lora_shrink_expand_launches")
     return st
+
+
+def lora_probe_read(src, workgroups: int, sink, stream=None) -> None:
+    """Measurement aid: one streaming read of every byte of the device tensor
+    `src` by `workgroups` workgroups (sink: device float32 [>= workgroups])."""
+    import torch
+    _need(src.is_cuda and src.is_contiguous(), LORA_ERR_SHAPE, "lora_probe_read", "src must be a contiguous device tensor")
+    _need(sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= workgroups, LORA_ERR_SHAPE,
+          "lora_probe_read", "sink must be a device float32 tensor of >= workgroups elements")
+    nbytes = src.numel() * src.element_size()
+    _check(_lib().lora_probe_read(src.data_ptr(), nbytes, int(workgroups), sink.data_ptr(), _stream(stream)),
+           "lora_probe_read")
+
+
+def lora_probe_empty(workgroups: int, stream=None) -> None:
+    """Measurement aid: one launch of `workgroups` workgroups that do nothing."""
+    _check(_lib().lora_probe_empty(int(workgroups), _stream(stream)), "lora_probe_empty")
 
 
 def _check(st: int, where: str) -> None:
@@ -312,8 +336,10 @@ def lora_expand(buf, lora_b: Sequence, bias: Optional[Sequence], y, meta: LoraMe
 def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], buf, y,
                        meta: LoraMeta, scale: float, offset_start: int = 0, add_inputs: bool = True,
                        stream=None) -> None:
-    """lora_shrink then lora_expand on the same buffer, in one call (one
-    launch for decode-like batches).  Arguments as for the two calls."""
+    """add_lora_linear in one call (one launch for decode-like batches): buf
+    is written as a fresh buffer, buf[i][t] = scale * x[t] @ lora_a[i][id_t]^T
+    (its entry contents are ignored, rows of -1 tokens untouched), then y as
+    lora_expand computes it.  Arguments as for the two calls."""
     n, h = x.shape
     s, _, r = buf.shape
     _layer_checks("lora_shrink_expand", meta, n, x=x, lora_a=lora_a, lora_b=lora_b, bias=bias, buf=buf, y=y,
@@ -330,8 +356,8 @@ def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Seq
 def lora_prepare_shrink_expand(mapping, x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], buf, y,
                                meta: LoraMeta, scale: float, offset_start: int = 0, add_inputs: bool = True,
                                stream=None) -> None:
-    """lora_prepare_meta(mapping) then lora_shrink_expand, in one call (one
-    launch for small decode-like batches)."""
+    """lora_prepare_meta(mapping) then lora_shrink_expand (buf written as a
+    fresh buffer), in one call (one launch for small decode-like batches)."""
     import torch
     n = mapping.numel()
     _, h = x.shape

@@ -105,7 +105,7 @@ size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
     const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
     return 2 * tok + 2 * round_up(sizeof(int32_t) * (max_loras + 1)) +
            round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign +
-           round_up(sizeof(int32_t) * (size_t)fused_sync_words(max_num_tokens, max_loras + 1));
+           round_up(sizeof(int32_t) * (size_t)fused_region_words(max_num_tokens, max_loras + 1));
 }
 
 int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out) {
@@ -144,6 +144,17 @@ int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, l
 
 namespace {
 
+// The fused calls' accumulation area: after the counters, at an offset fixed
+// by the sizes the region was bound for.
+float *fused_acc(const lora_meta_t *meta) {
+    return reinterpret_cast<float *>(meta->sync + fused_acc_offset(meta->max_num_tokens, meta->max_loras + 1));
+}
+
+// The LoRA-major kernel's part slots, after the accumulation area.
+float *fused_slots(const lora_meta_t *meta) {
+    return reinterpret_cast<float *>(meta->sync + fused_sync_words(meta->max_num_tokens, meta->max_loras + 1));
+}
+
 PrepareArgs prepare_args(const int32_t *mapping, int num_tokens, const lora_meta_t *meta) {
     PrepareArgs a;
     a.mapping = mapping;
@@ -155,7 +166,10 @@ PrepareArgs prepare_args(const int32_t *mapping, int num_tokens, const lora_meta
     a.no_lora = meta->no_lora_flag;
     a.status = meta->status;
     a.sync = meta->sync;
-    a.sync_tiles = fused_batch(num_tokens, meta->max_loras + 1) ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
+    const bool fused = fused_batch(num_tokens, meta->max_loras + 1);
+    a.sync_tiles = fused ? (int32_t)fused_tiles(num_tokens, meta->max_loras + 1) : 0;
+    a.acc = fused_acc(meta);
+    a.acc_floats = fused ? (int32_t)fused_acc_floats(num_tokens) : 0;
     a.num_tokens = num_tokens;
     a.max_loras = meta->max_loras;
     return a;
@@ -329,12 +343,14 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
     st = expand_args(buf, num_tokens, rank, lora_b, bias, slice_widths, num_slices, y, ldy, offset_start,
                      add_inputs, meta, ea, skip);
     if (st || skip) return st;
+    sa.overwrite = 1;   // add_lora_linear's buffer is a fresh one: buf = shrink
     const bool fused_allowed = env_int("LORA_FUSED") >= 0;   // LORA_FUSED=-1: always two launches
     if (fused_allowed) {
         // test knobs: polls before a waiter helps (default 128), owners leaving
         // their parts to the waiters (forces the helping path)
         const int help = getenv("LORA_FUSED_HELP_AFTER") ? env_int("LORA_FUSED_HELP_AFTER") : 128;
-        const hipError_t e = launch_fused(sa, ea, meta->token_lora_mapping, meta->max_loras, meta->sync, meta->status,
+        const hipError_t e = launch_fused(sa, ea, meta->token_lora_mapping, meta->max_loras, meta->sync, fused_acc(meta),
+                                          fused_slots(meta), meta->status,
                                           help, env_int("LORA_FUSED_OWNERS_SKIP"), stream);
         if (e == hipSuccess) return LORA_OK;
         if (e != hipErrorNotSupported) return LORA_ERR_LAUNCH;
@@ -344,15 +360,18 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
     return LORA_OK;
 }
 
-int lora_shrink_expand_launches(int num_tokens, int max_loras, int num_slices, int rank, int with_prepare) {
+int lora_shrink_expand_launches(int num_tokens, int max_loras, int hidden, int num_slices, int rank,
+                                int with_prepare) {
     if (num_tokens < 1 || num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
     if (max_loras < 1 || max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
     if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_SLICES;
     if (rank < 8 || rank > LORA_MAX_RANK || rank % 8) return LORA_ERR_SHAPE;
+    if (hidden < 8 || hidden % 8) return LORA_ERR_SHAPE;
     if (env_int("LORA_FUSED") >= 0 &&
         one_launch_range(num_tokens, (long)max_loras + 1, num_slices * rank, rank, with_prepare != 0))
         return 1;
-    return with_prepare ? 3 : 2;
+    return (with_prepare ? 1 : 0) +
+           shrink_launches(num_tokens, max_loras + 1, num_slices * rank, hidden, true, shrink_tuning()) + 1;
 }
 
 int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const void *x, int64_t ldx, int hidden,
@@ -377,7 +396,7 @@ int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const voi
     if (!skip && env_int("LORA_FUSED") >= 0) {
         const int help = getenv("LORA_FUSED_HELP_AFTER") ? env_int("LORA_FUSED_HELP_AFTER") : 128;
         const hipError_t e = launch_prepare_fused(prepare_args(mapping, num_tokens, meta), sa, ea, meta->sync,
-                                                  meta->status, help, env_int("LORA_FUSED_OWNERS_SKIP"), stream);
+                                                  fused_acc(meta), fused_slots(meta), meta->status, help, env_int("LORA_FUSED_OWNERS_SKIP"), stream);
         if (e == hipSuccess) {
             if ((st = mirror_flag(meta, stream))) return st;
             meta->num_tokens = num_tokens;

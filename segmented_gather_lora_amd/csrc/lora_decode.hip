@@ -12,11 +12,15 @@
 // Roles of id L:
 //   - idx < parts: shrink part idx -- K chunk idx of all S*r weight rows, for
 //     every token of L (the chunk's weights stay in registers across the
-//     16-token tiles); its sums go into buf with float atomics and the part
-//     is counted done on L's counter words;
+//     16-token tiles); its partial sums are stored in part slot idx (plain
+//     stores, no atomics: each slot has one writer) and the part is counted
+//     done on L's counter words;
 //   - idx >= parts: expand block idx - parts (and every (W - parts)-th after
-//     it) -- waits until L's parts are all done, then multiplies each tile's
-//     buffer rows by the block's weights and adds the result into y.
+//     it) -- waits until L's parts are all done, adds up each tile's rows of
+//     the part slots in part order (so buf is deterministic), multiplies them
+//     by the block's weights and adds the result into y; the expander of each
+//     slice's first block writes the rows to buf, which the call writes as a
+//     fresh buffer ("=").
 // Counter words, the wait, the help path of a waiter that sees no progress
 // and the reset by the last workgroup out are those of the tile-major kernel,
 // with the words of id L in place of those of tile L.
@@ -43,6 +47,9 @@ namespace {
 constexpr int kFilterSteps = kPrepMaxTokens / kThreads;   // 64-token steps per wave
 constexpr int kMaxChunk = 2 * kWaves * 64;                // K per part: two 64-wide steps per wave
 constexpr int kKeyWords = (LORA_MAX_LORAS + 1 + 31) / 32;   // presence bits of keys 0..max_loras
+constexpr int kRowsStride = 64 + 4;                         // fp32 per staged row (rank <= 64), padded
+constexpr int kSlotElems = (kTile * 64 + kThreads - 1) / kThreads;   // tile elements per thread, at most
+constexpr int kSlotBatch = 8;                               // part slots loaded per round trip
 
 // The batch's ids, one round trip: wave w holds the contiguous run of steps*64
 // tokens from t0 (so wave order is batch order), lane l token t0 + 64 q + l.
@@ -186,6 +193,7 @@ void lora_major_kernel(FusedArgs f) {
     __shared__ int s_claim;
     __shared__ uint32_t s_bits[kKeyWords];
     __shared__ floatx4 red[kWaves * MT * kWave];
+    __shared__ __attribute__((aligned(16))) float s_rows[kTile * kRowsStride];   // a tile's rows of one slice
 
     prefetch_kernargs<FusedArgs>();
     const ShrinkArgs &a = f.s;
@@ -219,6 +227,10 @@ void lora_major_kernel(FusedArgs f) {
     int32_t *const parts_done = words + kFusedPartsDone;
     int32_t *const past_wait = words + kFusedPastWait;
     int32_t *const flags = words + kFusedFlags;
+
+    // part slot p of this call: [p][S][N][r]
+    const int nsl = a.rows / rank;
+    auto slot_at = [&](int p, int i, int tok) { return f.slots + (((int64_t)p * nsl + i) * n + tok) * rank; };
 
     if (idx < nparts) {
         // ================ shrink part idx: K chunk idx of all weight rows of L
@@ -308,7 +320,8 @@ void lora_major_kernel(FusedArgs f) {
                         const int row = mt * 16 + 4 * (l >> 4) + c;
                         if (pr < cnt && row < a.rows) {
                             const int i = row / rank, j = row - i * rank;
-                            unsafeAtomicAdd(a.buf + ((int64_t)i * n + tk) * rank + j, v * a.scale);
+                            __hip_atomic_store(slot_at(idx, i, tk) + j, v * a.scale, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
                         }
                     }
                 }
@@ -389,6 +402,40 @@ void lora_major_kernel(FusedArgs f) {
     if (cnt == 0) return;   // the whole workgroup: no word of L is touched by anyone
     const int ntiles = (cnt + kTile - 1) / kTile;
 
+    // Rows of tile t of slice i (16 tokens x rank fp32): each thread takes
+    // up to kSlotElems (token, k) elements and adds up their part slots in
+    // part order; the loads of up to kSlotBatch parts are issued before the
+    // first add (indices past the last part re-read the last part's slot and
+    // add zero).
+    auto sum_slots = [&](int i, int t, bool writer) {
+        __syncthreads();   // the previous tile's rows have been read
+        const int elems = kTile * rank;
+#pragma unroll
+        for (int q = 0; q < kSlotElems; ++q) {
+            const int e = tid + q * kThreads;
+            if (e < elems) {
+                const int row = e / rank, j = e - row * rank;
+                const int pr = t * kTile + row;
+                const int tk = token_at(pr);
+                float v = 0.f;
+                for (int p0 = 0; p0 < nparts; p0 += kSlotBatch) {   // one round for up to 8 parts
+                    float vals[kSlotBatch];
+#pragma unroll
+                    for (int p = 0; p < kSlotBatch; ++p) {
+                        const int pp = p0 + p < nparts ? p0 + p : nparts - 1;
+                        vals[p] = __hip_atomic_load(slot_at(pp, i, tk) + j, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int p = 0; p < kSlotBatch; ++p) v += p0 + p < nparts ? vals[p] : 0.f;
+                }
+                s_rows[row * kRowsStride + j] = v;
+                if (writer && pr < cnt) a.buf[((int64_t)i * n + tk) * rank + j] = v;
+            }
+        }
+        __syncthreads();
+    };
+
     // A waiter's copy of part `ks` (rare; kept small so that it costs the main
     // path no registers): one fp32 dot product per (token, weight row).
     auto help_part = [&](int ks) {
@@ -409,7 +456,7 @@ void lora_major_kernel(FusedArgs f) {
                     sum += bf16_bits_to_float(xq[c] >> 16) * bf16_bits_to_float(aq[c] >> 16);
                 }
             }
-            unsafeAtomicAdd(a.buf + ((int64_t)i * n + tok) * rank + j, sum * a.scale);
+            __hip_atomic_store(slot_at(ks, i, tok) + j, sum * a.scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // every thread's additions have completed before the part is counted
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -468,18 +515,26 @@ void lora_major_kernel(FusedArgs f) {
         const float bias2 = bf16_bits_to_float(braw[1] & 0xffffu), bias3 = bf16_bits_to_float(braw[1] >> 16);
         for (int t = 0; t < ntiles; ++t) {
             if (blk != e0 || t != 0) load_y(t);
-            // the tile's buffer rows of this block's slice, as the A operand
-            // (device-coherent loads: buf was written by other workgroups' atomics)
-            const float *src = e.buf + ((int64_t)bk.i * n + token_at(t * kTile + n16)) * rank;
+            // the tile's rows of this block's slice: the sum of the parts' slots in
+            // part order (so buf is deterministic), gathered once per workgroup
+            // with device-coherent loads (other workgroups stored them) and
+            // shared through LDS; the expander of the slice's first block also
+            // writes them to the caller's buffer (buf = shrink)
+            sum_slots(bk.i, t, blk == f.block_begin[bk.i]);
             u32x4 ah[KS], al[KS];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 const int kk = k * 32 + 8 * g;
                 float v[8];
+                if (kk < rank) {
+                    const floatx4 lo4 = *reinterpret_cast<const floatx4 *>(&s_rows[n16 * kRowsStride + kk]);
+                    const floatx4 hi4 = *reinterpret_cast<const floatx4 *>(&s_rows[n16 * kRowsStride + kk + 4]);
+                    v[0] = lo4[0]; v[1] = lo4[1]; v[2] = lo4[2]; v[3] = lo4[3];
+                    v[4] = hi4[0]; v[5] = hi4[1]; v[6] = hi4[2]; v[7] = hi4[3];
+                } else {
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    v[c] = kk < rank ? __hip_atomic_load(src + kk + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : 0.f;
+                    for (int c = 0; c < 8; ++c) v[c] = 0.f;
+                }
                 uint32_t h[8], l[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
@@ -555,7 +610,7 @@ hipError_t launch_lora_major(const FusedArgs &fin, bool prepare, hipStream_t str
         const int want = atoi(v);
         if (want > parts) parts = want;
     }
-    if (parts > kFusedMaxParts) return hipErrorNotSupported;
+    if (parts > kLmMaxParts) return hipErrorNotSupported;   // the part slots hold this many
     int chunk = (fin.s.hidden + parts - 1) / parts;
     chunk = (chunk + 63) / 64 * 64;
     parts = (fin.s.hidden + chunk - 1) / chunk;

@@ -13,6 +13,8 @@ struct FusedArgs {
     ExpandArgs e;
     PrepareArgs p;          // the batch's mapping and metadata outputs (PREP kernels)
     int32_t *sync;
+    float *acc;             // the accumulation area (zero on entry; left zero)
+    float *slots;           // the LoRA-major kernel's part slots [part][S][N][r]
     int32_t *status;
     int32_t blocks;         // expand column blocks per tile (all slices)
     int32_t block_begin[LORA_MAX_SLICES + 1];   // prefix of column blocks per slice

@@ -246,11 +246,41 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
     const int step = shared ? total : grid;
     const int idx = shared ? b / total : 0;
 
+    // A workgroup counts out of a tile (thread 0, `out` = the count before
+    // its own) once it is done with the tile's parts, waits and reads of the
+    // accumulation area, and acts on the result at the tile's end, so the
+    // round trip overlaps its expand blocks.  The tile's last workgroup out
+    // clears the tile's rows of that area (every add into them has completed:
+    // each reader waited for all parts) and resets the tile's words, so the
+    // call leaves both at zero.
+    auto count_out = [&](int32_t *words) {
+        return __hip_atomic_fetch_add(words + kFusedPastWait, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto finish_tile = [&](const TileRef &tr, int32_t *words, int W, int out) {
+        if (tid == 0) s_claim = out == W - 1;
+        __syncthreads();
+        const bool last = s_claim;
+        __syncthreads();
+        if (!last) return;
+        const int per_tok = rank / 4;   // 16-byte pieces per token row of a slice
+        for (int x = tid; x < a.rows / 4 * kTile; x += kThreads) {
+            const int prow = x / (a.rows / 4), rest = x % (a.rows / 4);
+            const int si = rest / per_tok, piece = rest % per_tok;
+            const int pp = tr.tile * kTile + prow;
+            if (pp >= tr.seg_count) continue;
+            const int tt = sorted_at(a.meta, smem, tr.seg_start + pp);
+            if ((unsigned)tt >= (unsigned)a.num_tokens) continue;
+            float *dst = f.acc + ((int64_t)si * a.num_tokens + tt) * rank + 4 * piece;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) __hip_atomic_store(dst + k, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (tid == 0) reset_tile(words, a.k_splits);
+    };
+
     for (int tile = first; tile < total; tile += step) {
         const int W = shared ? grid / total + (tile < grid % total ? 1 : 0) : 1;
         int32_t *const words = f.sync + kFusedTileWords * tile;
         int32_t *const parts_done = words + kFusedPartsDone;
-        int32_t *const past_wait = words + kFusedPastWait;
         int32_t *const flags = words + kFusedFlags;
         const TileRef tr = lookup_tile(smem, nslots, tile);
 
@@ -340,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                     const int row0 = mt * 16 + 4 * g;
                     if (!tv || row0 >= a.rows) continue;
                     const int i = row0 / rank, j = row0 - i * rank;
-                    float *dst = a.buf + ((int64_t)i * a.num_tokens + tok) * rank + j;
+                    float *dst = f.acc + ((int64_t)i * a.num_tokens + tok) * rank + j;
                     const floatx4 v = acc[mt] * a.scale;
                     unsafeAtomicAdd(dst + 0, v[0]);
                     unsafeAtomicAdd(dst + 1, v[1]);
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                         sum += bf16_bits_to_float(xv[c] >> 16) * bf16_bits_to_float(av[c] >> 16);
                     }
                 }
-                unsafeAtomicAdd(a.buf + ((int64_t)i * a.num_tokens + tok) * rank + j, sum * a.scale);
+                unsafeAtomicAdd(f.acc + ((int64_t)i * a.num_tokens + tok) * rank + j, sum * a.scale);
             }
             // every thread's additions have completed before the part is counted
             __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -398,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
 
         // ---------------- 2. expand blocks idx, idx + W, ... of the tile
         bool waited = false;
+        int out = -1;   // thread 0: this workgroup's count-out result
         for (int blk = idx; blk < f.blocks; blk += W) {
             int i = 0;
 #pragma unroll
@@ -477,12 +508,17 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                     int pp = tr.tile * kTile + prow;
                     pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
                     int tt = sorted_at(e.meta, smem, tr.seg_start + pp);
-                    tt = (unsigned)tt < (unsigned)e.num_tokens ? tt : e.num_tokens - 1;
-                    const float *src = e.buf + ((int64_t)si * e.num_tokens + tt) * rank + 4 * piece;
+                    const bool tok_ok = (unsigned)tt < (unsigned)e.num_tokens;
+                    tt = tok_ok ? tt : e.num_tokens - 1;
+                    const int64_t o_acc = ((int64_t)si * e.num_tokens + tt) * rank + 4 * piece;
                     floatx4 bv;
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        bv[k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        bv[k] = __hip_atomic_load(f.acc + o_acc + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    // the call's result in the caller's buffer (buf = shrink), written by
+                    // one workgroup of the tile; rows past the segment repeat its last
+                    // token and store the same values
+                    if (idx == 0 && tok_ok) *reinterpret_cast<floatx4 *>(a.buf + o_acc) = bv;
                     uint32_t h[4], l[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -501,12 +537,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                     }
                 }
                 __syncthreads();
-                // done with parts and waits: the tile's last such workgroup
-                // resets its words (no exchange, count or poll of them is left)
-                if (tid == 0) {
-                    const int d = __hip_atomic_fetch_add(past_wait, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (d == W - 1) reset_tile(words, a.k_splits);
-                }
+                // done with parts, waits and reads of the accumulation area
+                if (tid == 0) out = count_out(words);
             }
 
             if (has_cols) {
@@ -550,11 +582,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                 }
             }
         }
-        if (!waited && tid == 0) {
-            // no expand block here: this workgroup is done with its parts, count it out
-            const int d = __hip_atomic_fetch_add(past_wait, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == W - 1) reset_tile(words, a.k_splits);
-        }
+        // no expand block here: this workgroup is done with its parts, count it out
+        if (!waited && tid == 0) out = count_out(words);
+        finish_tile(tr, words, W, out);
         __syncthreads();   // the staged rows are rewritten for the next tile
     }
 }
@@ -584,8 +614,8 @@ FusedFn pick(int mt, int ks, bool add) {
 // chunks of 64-multiples until about 256 shrink parts exist, as for the direct
 // shrink kernel; the grid is what the device holds at once.
 static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const PrepareArgs *prep,
-                         const int32_t *mapping_copy, int max_loras, int32_t *sync, int32_t *status, int help_after,
-                         int owners_skip, hipStream_t stream) {
+                         const int32_t *mapping_copy, int max_loras, int32_t *sync, float *acc, float *slots,
+                         int32_t *status, int help_after, int owners_skip, hipStream_t stream) {
     const int n = sin.num_tokens;
     const int nslots = sin.meta.nslots;
     const int segs = nslots < n ? nslots : n;
@@ -597,6 +627,8 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
     f.e = ein;
     if (prep) f.p = *prep;
     f.sync = sync;
+    f.acc = acc;
+    f.slots = slots;
     f.status = status;
     f.help_after = help_after;
     f.owners_skip = owners_skip;
@@ -660,14 +692,17 @@ static hipError_t launch(const ShrinkArgs &sin, const ExpandArgs &ein, const Pre
 }
 
 hipError_t launch_fused(const ShrinkArgs &sin, const ExpandArgs &ein, const int32_t *mapping_copy, int max_loras,
-                        int32_t *sync, int32_t *status, int help_after, int owners_skip, hipStream_t stream) {
-    return launch(sin, ein, nullptr, mapping_copy, max_loras, sync, status, help_after, owners_skip, stream);
+                        int32_t *sync, float *acc, float *slots, int32_t *status, int help_after, int owners_skip,
+                        hipStream_t stream) {
+    return launch(sin, ein, nullptr, mapping_copy, max_loras, sync, acc, slots, status, help_after, owners_skip,
+                  stream);
 }
 
 hipError_t launch_prepare_fused(const PrepareArgs &prep, const ShrinkArgs &sin, const ExpandArgs &ein,
-                                int32_t *sync, int32_t *status, int help_after, int owners_skip,
-                                hipStream_t stream) {
-    return launch(sin, ein, &prep, nullptr, prep.max_loras, sync, status, help_after, owners_skip, stream);
+                                int32_t *sync, float *acc, float *slots, int32_t *status, int help_after,
+                                int owners_skip, hipStream_t stream) {
+    return launch(sin, ein, &prep, nullptr, prep.max_loras, sync, acc, slots, status, help_after, owners_skip,
+                  stream);
 }
 
 }  // namespace lora

@@ -309,7 +309,9 @@ struct PrepareArgs {
     int32_t *no_lora;
     int32_t *status;
     int32_t *sync;        // work counters of the fused call, zeroed here
+    float *acc;           // the fused call's accumulation area, zeroed here
     int32_t sync_tiles;   // tiles whose counters the batch can use (0: none)
+    int32_t acc_floats;   // floats of the accumulation area the batch can use (0: none)
     int32_t num_tokens;
     int32_t max_loras;
 };
@@ -328,6 +330,7 @@ struct ShrinkArgs {
     int32_t k_splits;     // K chunks per tile
     int32_t k_chunk;      // elements of K per chunk (multiple of 64)
     int32_t num_units;    // tiles upper bound * row_blocks * k_splits
+    int32_t overwrite;    // 1: buf = result (a fresh buffer), 0: buf += result
     float scale;
 };
 
@@ -383,6 +386,10 @@ inline long persistent_grid(long units, long cap, const void *fn, int threads, s
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream_t s);
+// Kernel launches launch_shrink makes for these sizes (host only): 2 when a
+// fresh buffer (overwrite) is combined from K chunks and its rows are zeroed
+// first, else 1 (0 for an empty batch).
+int shrink_launches(int n, int nslots, int rows, int hidden, bool overwrite, const ShrinkTuning &cfg);
 hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream_t s);
 // Fused shrink -> expand for short segments.  Returns hipErrorNotSupported
 // (launching nothing) when the shape is outside the fused kernel's range; the
@@ -390,11 +397,13 @@ hipError_t launch_expand(const ExpandArgs &a, const ExpandTuning &cfg, hipStream
 // batch's id copy (ids outside [-1, max_loras) already -1), read by the
 // LoRA-major layout.
 hipError_t launch_fused(const ShrinkArgs &s, const ExpandArgs &e, const int32_t *mapping_copy, int max_loras,
-                        int32_t *sync, int32_t *status, int help_after, int owners_skip, hipStream_t stream);
+                        int32_t *sync, float *acc, float *slots, int32_t *status, int help_after, int owners_skip,
+                        hipStream_t stream);
 // The same with the batch's prepare done inside the launch (at most 2048
 // tokens); hipErrorNotSupported likewise.
 hipError_t launch_prepare_fused(const PrepareArgs &p, const ShrinkArgs &s, const ExpandArgs &e, int32_t *sync,
-                                int32_t *status, int help_after, int owners_skip, hipStream_t stream);
+                                float *acc, float *slots, int32_t *status, int help_after, int owners_skip,
+                                hipStream_t stream);
 
 // The fused call serves batches of short segments only: fewer than 24
 // tokens per LoRA on average, so at most kFusedMaxTokens tokens.
@@ -410,7 +419,30 @@ inline long fused_tiles(long n, long nslots) {
     if (n > kFusedMaxTokens) n = kFusedMaxTokens;
     return (n + 15) / 16 + (nslots < n ? nslots : n) + 1;
 }
-inline long fused_sync_words(long n, long nslots) { return kFusedTileWords * fused_tiles(n, nslots); }
+// After the counters, the fp32 accumulation area of the fused calls: the
+// shrink parts add into it (it is laid out like buf, [S][N][r] with S*r <=
+// kFusedAccPerToken), the expand reads it, and the last reader of each tile
+// (or LoRA id) clears its rows again, so it is all zero between calls.
+constexpr int kFusedAccPerToken = 64;
+inline long fused_acc_floats(long n) { return kFusedAccPerToken * (n < kFusedMaxTokens ? n : kFusedMaxTokens); }
+inline long fused_sync_words(long n, long nslots) {
+    return kFusedTileWords * fused_tiles(n, nslots) + fused_acc_floats(n);
+}
+// Word offset of the accumulation area in a region bound for max_num_tokens.
+inline long fused_acc_offset(long max_num_tokens, long nslots) {
+    return kFusedTileWords * fused_tiles(max_num_tokens, nslots);
+}
+// After the accumulation area, the LoRA-major kernel's part slots: each
+// shrink part stores its partial sums in a slot of its own ([part][S][N][r],
+// S*r <= kFusedAccPerToken), and the expand adds the slots up, so that area
+// needs no clearing.  Batches of at most kLmMaxTokens tokens, at most
+// kLmMaxParts parts.
+constexpr int kLmMaxParts = 16;
+constexpr long kLmMaxTokens = 2048;
+inline long lm_slot_floats(long n) { return (long)kLmMaxParts * kFusedAccPerToken * (n < kLmMaxTokens ? n : kLmMaxTokens); }
+inline long fused_region_words(long max_num_tokens, long nslots) {
+    return fused_sync_words(max_num_tokens, nslots) + lm_slot_floats(max_num_tokens);
+}
 // Batches a fused call can take (by size alone): fewer than 24 tokens per
 // segment on average and at most kFusedMaxTokens tokens.  Only their
 // counters need zeroing by prepare.

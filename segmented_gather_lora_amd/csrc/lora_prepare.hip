@@ -40,8 +40,31 @@ constexpr int kRankMask = (1 << kRankBits) - 1;
 // scatter from one workgroup costs a partial cache-line write per token.
 constexpr int kLdsSorted = kSteps * kThreads;
 
+// 16-byte groups per tile of the fused call's counters: the exit count, the
+// done count and the part flags.
+constexpr int kSyncGroups = 2 + kFusedMaxParts / 4;
+
+// Workgroups 1.. of the launch: the fused call's counters and accumulation
+// area start every batch at zero (each fused call also leaves them zero),
+// cleared next to the sort instead of by the sorting workgroup.
+__device__ __forceinline__ void clear_fused_area(const PrepareArgs &a) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int stride = (gridDim.x - 1) * kThreads;
+    const int first = (blockIdx.x - 1) * kThreads + threadIdx.x;
+    for (int k = first; k < a.sync_tiles * kSyncGroups; k += stride) {
+        const int tile = k / kSyncGroups, w = k % kSyncGroups;
+        const int word = w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + 4 * (w - 2);
+        *reinterpret_cast<u32x4 *>(a.sync + kFusedTileWords * tile + word) = z;
+    }
+    for (int k = first; k < a.acc_floats / 4; k += stride) reinterpret_cast<u32x4 *>(a.acc)[k] = z;
+}
+
 __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     prefetch_kernargs<PrepareArgs>();
+    if (blockIdx.x > 0) {
+        clear_fused_area(a);
+        return;
+    }
     // per wave and key: the running count of the wave's slice (later its
     // base).  Wave-major, so the lanes of a step, which hold different keys,
     // reach different banks.
@@ -63,17 +86,6 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
     if (tid == 0) {
         s_any = 0;
         s_bad = 0;
-    }
-    // the fused call's counters start every batch at zero (each fused call
-    // also leaves them zero)
-    {   // per tile: the 16-byte groups holding the exit count, the done count and the part flags
-        constexpr int kGroups = 2 + kFusedMaxParts / 4;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int k = tid; k < a.sync_tiles * kGroups; k += kThreads) {
-            const int tile = k / kGroups, w = k % kGroups;
-            const int word = w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + 4 * (w - 2);
-            *reinterpret_cast<u32x4 *>(a.sync + kFusedTileWords * tile + word) = z;
-        }
     }
     __syncthreads();
 
@@ -231,8 +243,13 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
 
 }  // namespace
 
+// One sorting workgroup, plus workgroups that clear the fused call's area
+// (about 4 16-byte stores per thread) when the batch can use it.
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    const long groups = (long)a.sync_tiles * kSyncGroups + a.acc_floats / 4;
+    long clear = (groups + 4L * kThreads - 1) / (4L * kThreads);
+    if (clear > 64) clear = 64;
+    hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(1 + clear)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@
 // ragged K range is masked.  With a fixed number of loads per step the
 // compiler can wait for exactly the step being multiplied while the next one
 // is in flight.  Partial sums of the WK waves are added in LDS; K chunks are
-// combined with float atomics, else the unit does a read-modify-write of buf.
+// combined with float atomics, else the unit does a read-modify-write of buf
+// (or, for a fresh buffer, a plain store).
 #include "lora_internal.h"
 
 #include <stdlib.h>
@@ -209,6 +210,8 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
                         unsafeAtomicAdd(dst + 1, v[1]);
                         unsafeAtomicAdd(dst + 2, v[2]);
                         unsafeAtomicAdd(dst + 3, v[3]);
+                    } else if (a.overwrite) {
+                        *reinterpret_cast<floatx4 *>(dst) = v;
                     } else {
                         floatx4 o = *reinterpret_cast<floatx4 *>(dst);
                         o += v;
@@ -398,12 +401,42 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
                     unsafeAtomicAdd(dst + 1, v[1]);
                     unsafeAtomicAdd(dst + 2, v[2]);
                     unsafeAtomicAdd(dst + 3, v[3]);
+                } else if (a.overwrite) {
+                    *reinterpret_cast<floatx4 *>(dst) = v;
                 } else {
                     floatx4 o = *reinterpret_cast<floatx4 *>(dst);
                     o += v;
                     *reinterpret_cast<floatx4 *>(dst) = o;
                 }
             }
+        }
+    }
+}
+
+// Rows of the batch's active tokens set to zero, ahead of a split-K shrink
+// into a fresh buffer (its K chunks are added with atomics).  Rows of tokens
+// with id -1 are not touched.  Units are 16-token tiles.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(ShrinkArgs a) {
+    extern __shared__ int smem[];
+    __shared__ int s_wsum[kThreads / kWave];
+    const int nslots = a.meta.nslots;
+    const int total = build_tile_table<kThreads>(a.meta, 16, smem, s_wsum);
+    const int per_tok = a.rank / 4;              // 16-byte pieces per token row of a slice
+    const int per_unit = 16 * a.rows / 4;
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    const UnitWalker walk(total);
+    for (int jj = walk.first;; jj += walk.stride) {
+        const int u = walk.unit(jj);
+        if (u < 0) break;
+        const TileRef tr = lookup_tile(smem, nslots, u);
+        for (int x = threadIdx.x; x < per_unit; x += kThreads) {
+            const int prow = x / (a.rows / 4), rest = x % (a.rows / 4);
+            const int i = rest / per_tok, piece = rest % per_tok;
+            const int pp = tr.tile * 16 + prow;
+            if (pp >= tr.seg_count) continue;
+            const int t = a.meta.sorted[tr.seg_start + pp];
+            if ((unsigned)t >= (unsigned)a.num_tokens) continue;
+            *reinterpret_cast<floatx4 *>(a.buf + ((int64_t)i * a.num_tokens + t) * a.rank + 4 * piece) = z;
         }
     }
 }
@@ -472,20 +505,27 @@ constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 // long ones the LDS-staged kernel with a tile of 64-128 tokens x up to 192
 // rows.  K chunks (combined with float atomics) are added only when the units
 // would not cover the GPU.  `cfg` fields > 0 override the choice (tuning).
-hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStream_t s) {
-    ShrinkArgs a = in;
-    const int n = a.num_tokens;
-    const int nslots = a.meta.nslots;
-    const int mtiles = (a.rows + 15) / 16;
+namespace {
+
+struct ShrinkPlan {
+    bool staged;
+    ShrinkFn fn;
+    int tile_tokens, row_blocks, k_splits, k_chunk;
+    long units_upper;
+};
+
+ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuning &cfg) {
+    ShrinkPlan pl;
+    const int mtiles = (rows + 15) / 16;
     const int segs = nslots < n ? nslots : n;
     const int avg = (n + segs - 1) / segs;
-    const int max_ks = (a.hidden + 255) / 256;
+    const int max_ks = (hidden + 255) / 256;
 
-    bool staged = cfg.variant == 3 || (cfg.variant == 0 && avg >= 24);
-    int tile_tokens, rows_per_wg;
+    pl.staged = cfg.variant == 3 || (cfg.variant == 0 && avg >= 24);
+    int rows_per_wg;
     int forced_ks = cfg.k_splits;
-    ShrinkFn fn;
-    if (staged) {
+    int model_ks = 1;
+    if (pl.staged) {
         int idx = cfg.staged_cfg;
         if (idx <= 0 || idx > kNumStaged) {
             // Cost model: a unit streams (tokens + rows) x K_chunk bf16 through
@@ -498,30 +538,30 @@ hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStrea
                 if (!kStaged[c].automatic) continue;
                 const int T = 16 * kStaged[c].nt, R = 16 * kStaged[c].mr;
                 const double tiles = (double)segs * ((avg + T - 1) / T);
-                const double rb = (a.rows + R - 1) / R;
+                const double rb = (rows + R - 1) / R;
                 for (int ksc = 1; ksc <= 4; ksc *= 2) {
                     if (forced_ks > 0 && ksc != forced_ks) continue;
                     const double units = tiles * rb * ksc;
-                    const double per_unit = (double)(T + R) * 2.0 * ((a.hidden + ksc - 1) / ksc);
+                    const double per_unit = (double)(T + R) * 2.0 * ((hidden + ksc - 1) / ksc);
                     double cost = (units / cus > 1.0 ? units / cus : 1.0) * per_unit;
                     // waste on rows past S*r and tokens past the segment end
-                    cost *= (rb * R) / (double)a.rows;
-                    if (ksc > 1) cost += ksc * (double)n * a.rows * bytes_per_atomic / cus;
+                    cost *= (rb * R) / (double)rows;
+                    if (ksc > 1) cost += ksc * (double)n * rows * bytes_per_atomic / cus;
                     if (cost < best) {
                         best = cost;
                         idx = c;
-                        if (forced_ks <= 0) a.k_splits = ksc;
+                        model_ks = ksc;
                     }
                 }
             }
-            if (forced_ks <= 0) forced_ks = a.k_splits;
+            if (forced_ks <= 0) forced_ks = model_ks;
         } else {
             idx -= 1;
         }
         const StagedCfg &c = kStaged[idx];
-        tile_tokens = 16 * c.nt;
+        pl.tile_tokens = 16 * c.nt;
         rows_per_wg = 16 * c.mr;
-        fn = c.fn;
+        pl.fn = c.fn;
     } else {
         int nt = cfg.tile_tokens > 0 ? cfg.tile_tokens / 16 : (avg <= 16 ? 1 : (avg <= 32 ? 2 : 4));
         if (nt != 1 && nt != 2 && nt != 4) nt = 8;
@@ -531,33 +571,64 @@ hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStrea
         int mt = cfg.mtiles_per_wave > 0 ? cfg.mtiles_per_wave : (mtiles + wr - 1) / wr;
         if (mt > 4) mt = 4;
         if (nt == 8 && mt > 2) mt = 2;
-        tile_tokens = 16 * nt;
+        pl.tile_tokens = 16 * nt;
         rows_per_wg = wr * mt * 16;
-        fn = pick(nt, wk, mt);
+        pl.fn = pick(nt, wk, mt);
     }
-    a.row_blocks = (a.rows + rows_per_wg - 1) / rows_per_wg;
+    pl.row_blocks = (rows + rows_per_wg - 1) / rows_per_wg;
 
-    const int tiles_upper = (n + tile_tokens - 1) / tile_tokens + segs;
-    const int busy = ((n + tile_tokens - 1) / tile_tokens + (segs + 1) / 2) * a.row_blocks;
+    const int tiles_upper = (n + pl.tile_tokens - 1) / pl.tile_tokens + segs;
+    const int busy = ((n + pl.tile_tokens - 1) / pl.tile_tokens + (segs + 1) / 2) * pl.row_blocks;
     int ks = 1;
-    if (!staged && busy < 256) ks = (256 + busy - 1) / busy;
+    if (!pl.staged && busy < 256) ks = (256 + busy - 1) / busy;
     if (forced_ks > 0) ks = forced_ks;
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
-    int chunk = (a.hidden + ks - 1) / ks;
+    int chunk = (hidden + ks - 1) / ks;
     chunk = (chunk + 63) / 64 * 64;
-    ks = (a.hidden + chunk - 1) / chunk;
-    a.k_splits = ks;
-    a.k_chunk = chunk;
-    const long units_upper = (long)tiles_upper * a.row_blocks * ks;
-    a.num_units = (int)units_upper;
+    ks = (hidden + chunk - 1) / chunk;
+    pl.k_splits = ks;
+    pl.k_chunk = chunk;
+    pl.units_upper = (long)tiles_upper * pl.row_blocks * ks;
+    return pl;
+}
+
+}  // namespace
+
+int shrink_launches(int n, int nslots, int rows, int hidden, bool overwrite, const ShrinkTuning &cfg) {
+    if (n < 1) return 0;
+    return (overwrite && plan_shrink(n, nslots, rows, hidden, cfg).k_splits > 1) ? 2 : 1;
+}
+
+hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStream_t s) {
+    ShrinkArgs a = in;
+    const int n = a.num_tokens;
+    const int nslots = a.meta.nslots;
+    const ShrinkPlan pl = plan_shrink(n, nslots, a.rows, a.hidden, cfg);
+    a.row_blocks = pl.row_blocks;
+    a.k_splits = pl.k_splits;
+    a.k_chunk = pl.k_chunk;
+    a.num_units = (int)pl.units_upper;
+
+    if (a.overwrite && a.k_splits > 1) {
+        // a fresh buffer combined from K chunks with atomics: zero its rows first
+        ShrinkArgs z = a;
+        z.meta.lds_tokens = 0;
+        const size_t zlds = sizeof(int) * (size_t)(4 * nslots + 1);
+        const long zunits = (n + 15) / 16 + (nslots < n ? nslots : n);
+        const long zgrid = persistent_grid(zunits, 1024, reinterpret_cast<const void *>(zero_rows_kernel), kThreads,
+                                           zlds);
+        hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)zgrid), dim3(kThreads), zlds, s, z);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     // small batches: the direct-load kernel keeps the sorted indices in LDS
-    a.meta.lds_tokens = (!staged && n <= kLdsTokensMax) ? n : 0;
+    a.meta.lds_tokens = (!pl.staged && n <= kLdsTokensMax) ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
-    const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : (staged ? 512 : 1024),
-                                      reinterpret_cast<const void *>(fn), kThreads, lds);
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+    const long grid = persistent_grid(pl.units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : (pl.staged ? 512 : 1024),
+                                      reinterpret_cast<const void *>(pl.fn), kThreads, lds);
+    hipLaunchKernelGGL(pl.fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@ from _numeric import bits_to_f64
 
 SHRINK_RTOL = 1e-3
 EXPAND_RTOL = 2e-2
+# Fill of the fp32 buffer handed to the one-launch calls: they write it as a
+# fresh buffer ("=", add_lora_linear's zeroed buffer), so active rows must not
+# depend on it and rows of -1 tokens must keep it bit for bit.
+BUF_POISON = 12345.6789
 
 
 def lib():
@@ -189,7 +193,7 @@ def poison_meta(meta) -> None:
 
 def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int | None = None,
                   seed: int = 0, offset_start: int = 0, ldy_extra: int = 0, fused: bool = False,
-                  prep: bool = False) -> dict:
+                  prep: bool = False, nthreads: int = 8) -> dict:
     """prepare + (shrink, expand) per layer on the GPU -- or the one
     lora_shrink_expand call per layer with `fused`, and with `prep` the first
     layer's call also prepares the batch (lora_prepare_shrink_expand, on
@@ -218,10 +222,11 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         S, r, O = len(sp.slices), sp.rank, sum(sp.slices)
         if sp.expand_only:
             buf = D.x.clone()
+        elif fused:
+            buf = torch.full((S, n, r), BUF_POISON, dtype=torch.float32, device="cuda")
         else:
             buf = torch.zeros((S, n, r), dtype=torch.float32, device="cuda")
-            if not fused:
-                sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
+            sgl.lora_shrink(D.x, D.a, buf, meta, sp.scale)
         ldy = offset_start + O + ldy_extra
         y0full = torch.zeros((n, ldy), dtype=torch.bfloat16)
         y0full[:, offset_start:offset_start + O] = L.y0
@@ -252,14 +257,18 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         if sp.expand_only:
             assert np.array_equal(buf_g, L.x.numpy()), "expand modified its input"
         else:
-            assert np.all(buf_g[:, neg, :] == 0), "shrink touched a -1 row"
+            fill = np.float32(BUF_POISON) if fused else np.float32(0.0)
+            assert np.all(buf_g[:, neg, :] == fill), "shrink touched a -1 row"
         assert np.array_equal(y_g[neg], y0b[neg]), "expand touched a -1 row"
         assert np.array_equal(y_g[:, :offset_start], y0b[:, :offset_start])
         assert np.array_equal(y_g[:, offset_start + O:], y0b[:, offset_start + O:])
         # oracle on the sample
         buf_ref, y_ref, bound, mag = oracle_layer(L, mapping, ml, tokens, add_inputs, y_in=y0b,
-                                                  offset_start=offset_start)
-        sr = shrink_check(buf_g[:, tokens], buf_ref, bound)
+                                                  offset_start=offset_start, nthreads=nthreads)
+        # rows of -1 tokens were checked bit for bit above; a fresh buffer's
+        # stay as they were, so the oracle's zero rows are not compared
+        act = ~neg[tokens]
+        sr = shrink_check(buf_g[:, tokens][:, act], buf_ref[:, act], bound[:, act])
         extra = propagated(L, mapping[tokens], buf_ref, bound)
         cols = slice(offset_start, offset_start + O)
         ex = expand_check(y_g[tokens][:, cols], y_ref[:, cols], y0b[tokens][:, cols], mag, add_inputs, extra)
@@ -277,12 +286,17 @@ def sync_words(n: int, max_loras: int) -> int:
 
 
 def check_sync_clear(meta, n: int) -> None:
-    """Every fused call leaves its counters at zero and reports no timeout."""
+    """Every fused call leaves its counters and its accumulation area (after
+    the counters of a region bound for max_num_tokens: 64 floats per token)
+    at zero, and reports no timeout."""
     v = meta.views()
     off = meta.struct.sync - meta.region.data_ptr()
     words = meta.region[off:off + 4 * sync_words(n, meta.max_loras)].view(torch.int32).cpu().numpy()
     counters = words.reshape(-1, 128)[:, [0, 32] + list(range(64, 128))]
     assert np.all(counters == 0), "fused counters not reset: %s" % counters[np.any(counters != 0, axis=1)][:4]
+    acc_off = off + 4 * sync_words(meta.max_num_tokens, meta.max_loras)
+    acc = meta.region[acc_off:acc_off + 4 * 64 * min(n, 24576)].view(torch.int32).cpu().numpy()
+    assert np.all(acc == 0), "accumulation area not cleared: %d nonzero words" % int((acc != 0).sum())
     assert int(v["status"][0]) in (0, lib().LORA_ERR_ID_RANGE), "status %d" % int(v["status"][0])
 
 

@@ -16,11 +16,12 @@ def _library_built():
     _build.ensure_built()
 
 
-def _wl(n, max_loras, layers):
+def _wl(n, max_loras, layers, hidden=4096):
     """A stand-in workload: n tokens, max_loras, and (slices, rank) per layer."""
     mapping = types.SimpleNamespace(numel=lambda: n)
     spec = types.SimpleNamespace(max_loras=max_loras)
-    ls = [types.SimpleNamespace(spec=types.SimpleNamespace(slices=s, rank=r, expand_only=False)) for s, r in layers]
+    ls = [types.SimpleNamespace(spec=types.SimpleNamespace(slices=s, rank=r, hidden=hidden, expand_only=False))
+          for s, r in layers]
     return types.SimpleNamespace(mapping=mapping, spec=spec, layers=ls)
 
 
@@ -28,13 +29,20 @@ def test_launch_count_query():
     """The library's own answer (host only) at the edges of the one-launch range."""
     import segmented_gather_lora_amd as sgl
     q = sgl.lora_shrink_expand_launches
-    assert q(256, 32, 3, 16, True) == 1 and q(256, 32, 3, 16, False) == 1
-    assert q(2048, 1022, 3, 16, True) == 1 and q(2049, 1022, 3, 16, True) == 3
-    assert q(2049, 1022, 3, 16, False) == 1
-    assert q(23 * 33, 32, 3, 16, False) == 1 and q(23 * 33 + 1, 32, 3, 16, False) == 2
-    assert q(256, 32, 1, 64, False) == 1 and q(256, 32, 1, 72, False) == 2 and q(256, 32, 3, 32, False) == 2
-    assert q(23 * 1024, 1023, 1, 8, False) == 1 and q(23 * 1024 + 1, 1023, 1, 8, False) == 2
-    for bad in [(0, 32, 3, 16), (256, 0, 3, 16), (256, 32, 0, 16), (256, 32, 3, 12)]:
+    assert q(256, 32, 4096, 3, 16, True) == 1 and q(256, 32, 4096, 3, 16, False) == 1
+    assert q(2048, 1022, 4096, 3, 16, True) == 1 and q(2049, 1022, 4096, 3, 16, True) == 3
+    assert q(2049, 1022, 4096, 3, 16, False) == 1
+    # outside the range: shrink + expand, plus the zeroing of buf's rows when the shrink is split over K
+    sep = (2, 3)
+    assert q(23 * 33, 32, 4096, 3, 16, False) == 1 and q(23 * 33 + 1, 32, 4096, 3, 16, False) in sep
+    assert q(256, 32, 4096, 1, 64, False) == 1 and q(256, 32, 4096, 1, 72, False) in sep
+    assert q(256, 32, 4096, 3, 32, False) in sep
+    assert q(23 * 1024, 1023, 4096, 1, 8, False) == 1 and q(23 * 1024 + 1, 1023, 4096, 1, 8, False) in sep
+    assert q(16384, 128, 8192, 3, 128, False) == 2 and q(16384, 128, 8192, 3, 128, True) == 3
+    # a split-K shrink into a fresh buffer zeroes the active rows first (Zipf's down layer)
+    assert q(4096, 64, 14336, 1, 32, False) == 3 and q(4096, 64, 14336, 1, 32, True) == 4
+    for bad in [(0, 32, 4096, 3, 16), (256, 0, 4096, 3, 16), (256, 32, 4096, 0, 16), (256, 32, 4096, 3, 12),
+                (256, 32, 12, 3, 16)]:
         with pytest.raises(sgl.LoraError):
             q(*bad, True)
 
@@ -54,6 +62,80 @@ def test_one_launch_range():
     assert not bench.one_launch(_wl(256, 32, [((64,), 72)]), 0, False)
     assert not bench.one_launch(_wl(256, 32, [((64, 64, 64), 32)]), 0, False)
     assert not bench.one_launch(_wl(0, 32, qkv16), 0, False)
+
+
+def test_gpus_above_one_exits_with_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_formulas():
+    """Per-call bytes from the step's definition on a hand-checkable case."""
+    import torch
+    m = torch.tensor([0, -1, 1, 0, 2, -1], dtype=torch.int32)
+    L = types.SimpleNamespace(spec=types.SimpleNamespace(slices=(16, 8), rank=8, hidden=32, expand_only=False),
+                              bias=None)
+    wl = types.SimpleNamespace(mapping=m, layers=[L])
+    ab = bench.algorithmic_bytes(wl)
+    ta, la, S, r, H, O = 4, 3, 2, 8, 32, 24
+    assert ab["T_a"] == ta and ab["L_a"] == la and ab["prepare"] == 12 * 6
+    assert ab["shrink"] == [2 * ta * H + 2 * la * S * r * H + 8 * S * ta * r]
+    assert ab["shrink_fresh"] == [2 * ta * H + 2 * la * S * r * H + 4 * S * ta * r]
+    assert ab["expand"] == [4 * S * ta * r + 2 * la * r * O + 2 * ta * O * 2]
+
+
+def test_plan_merges_and_replays():
+    p = bench.Plan()
+    p.workload, p.phase = "w", "timed"
+    p.replay([("preplinear0", 3), ("linear1", 2)], 2)
+    p.add("expand0", 1, times=4)
+    assert p.calls == [["w", "timed", "preplinear0", 3, 1], ["w", "timed", "linear1", 2, 1],
+                       ["w", "timed", "preplinear0", 3, 1], ["w", "timed", "linear1", 2, 1],
+                       ["w", "timed", "expand0", 1, 4]]
+
+
+def _write_trace(path, names_durations):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 1000
+        for i, (name, dur) in enumerate(names_durations):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 500
+
+
+def test_summarize_trace_matches_plan(tmp_path):
+    """Library dispatches (foreign kernels ignored) matched one by one with the
+    plan; per workload, phase, call and kernel averages."""
+    plan = {"calls": [["zipf", "warmup", "preplinear0", 3, 1],
+                      ["zipf", "timed", "preplinear0", 3, 1], ["zipf", "timed", "linear1", 3, 1],
+                      ["zipf", "timed", "preplinear0", 3, 1], ["zipf", "timed", "linear1", 3, 1],
+                      ["decode", "per_call", "preplinear0", 1, 2]]}
+    json.dump(plan, open(tmp_path / "plan.json", "w"))
+    P, Z = "void lora::prepare_kernel(lora::PrepareArgs)", "void lora::zero_rows_kernel(lora::ShrinkArgs)"
+    S0, S1 = "void lora::shrink_lds_kernel<4, 2, 2, 4>(lora::ShrinkArgs)", "void lora::shrink_lds_kernel<2,2,2,4>(x)"
+    E = "void lora::expand_kernel<1, 2, true, false>(lora::ExpandArgs)"
+    LM = "void lora::lora_major_kernel<3, 1, true, true>(lora::FusedArgs)"
+    rows = [(P, 7), (S0, 20), (E, 100), ("torch_fill", 3),
+            (P, 6), (S0, 24), (E, 110), (Z, 2), (S1, 40), (E, 30),
+            (P, 6), (S0, 26), (E, 130), (Z, 2), (S1, 44), (E, 34),
+            (LM, 13000), (LM, 15000)]
+    _write_trace(tmp_path / "t.csv", rows)
+    out = bench.summarize_trace(str(tmp_path / "t.csv"), str(tmp_path / "plan.json"), str(tmp_path / "o.md"), "cmd")
+    assert out["zipf/timed/preplinear0/shrink0"] == 0.025 and out["zipf/timed/preplinear0/expand0"] == 0.12
+    assert out["zipf/timed/linear1/expand1"] == 0.032 and out["zipf/timed/linear1/zero1"] == 0.002
+    assert out["zipf/timed/preplinear0/prepare"] == 0.006
+    assert out["decode/per_call/preplinear0/one_launch0"] == 14.0
+    assert not any(k.startswith("zipf/warmup") for k in out)
+
+
+def test_summarize_trace_rejects_a_mismatch(tmp_path):
+    json.dump({"calls": [["w", "timed", "shrink0", 1, 1]]}, open(tmp_path / "plan.json", "w"))
+    _write_trace(tmp_path / "t.csv", [("void lora::expand_kernel<1,1,true,true>(a)", 5)])
+    with pytest.raises(SystemExit):
+        bench.summarize_trace(str(tmp_path / "t.csv"), str(tmp_path / "plan.json"), str(tmp_path / "o.md"), "c")
 
 
 def _write_pmc(path, counter, rows):
@@ -92,19 +174,3 @@ def test_summarize_pmc_one_launch_call(tmp_path):
     out = tmp_path / "o.json"
     bench.summarize_pmc("decode", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out), "cmd")
     assert json.load(open(out))["traffic_bytes"] == {"preplinear0": 2 * 7 * 1024}
-
-
-def test_summarize_stats_names(tmp_path):
-    p = tmp_path / "s.csv"
-    with open(p, "w", newline="") as fh:
-        w = csv.writer(fh)
-        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
-        w.writerow(["void lora::(anonymous namespace)::expand_kernel<1, 1, true, true>(lora::ExpandArgs)",
-                    10, 80000, 8000, 30.0, 7000, 9000, 1])
-        w.writerow(["void lora::(anonymous namespace)::lora_major_kernel<3, 1, true, true>(lora::FusedArgs)",
-                    10, 130000, 13000, 70.0, 12000, 14000, 1])
-    out = tmp_path / "s.md"
-    bench.summarize_stats("decode", str(p), str(out), "cmd")
-    text = open(out).read()
-    assert "| lora::lora_major_kernel<3, 1, true, true> | 10 | 13.000 | 12.000 | 14.000 | 70.0 |" in text
-    assert text.index("lora_major_kernel") < text.index("expand_kernel")    # sorted by total time

@@ -16,6 +16,9 @@ import _harness as H
 
 pytestmark = pytest.mark.gpu
 
+# the oracle runs on every core this process may use
+NTHREADS = max(1, len(os.sched_getaffinity(0)))
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _setup():
@@ -133,8 +136,11 @@ def test_host_mirror_of_flag():
 
 @pytest.mark.parametrize("add_inputs", [True, False])
 @pytest.mark.parametrize("name,n", [("tiny", None), ("decode", 200), ("prefill", 600), ("zipf", 300),
-                                    ("large", 160)])
+                                    ("zipf", 1500), ("large", 160)])
 def test_parity_all_tokens(name, n, add_inputs):
+    """Every token at reduced N.  Zipf at 1500 tokens (about 23 per id at rank
+    32) takes the expand kernel of 32-token tiles walking runs of 4 column
+    blocks, the one the full Zipf shape runs."""
     wl = workloads.make_workload(name, num_tokens=n)
     print("parity", name, n, add_inputs, flush=True)
     st = H.run_and_check(wl, add_inputs=add_inputs)
@@ -146,6 +152,21 @@ def test_parity_full_size_sampled(name, sample):
     wl = workloads.make_workload(name)
     print("full size", name, flush=True)
     st = H.run_and_check(wl, add_inputs=True, sample=sample, seed=11)
+    print(st, flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name,add_inputs", [("prefill", True), ("prefill", False), ("zipf", True),
+                                             ("large", True), ("large", False)])
+def test_parity_full_size_every_token(name, add_inputs):
+    """Every token of the full-size workloads through the calls the bench
+    times (lora_prepare_shrink_expand for the first layer, lora_shrink_expand
+    for the next; the separate kernels at these shapes), checked against the
+    oracle on all host cores; add_inputs=false once per shape class."""
+    wl = workloads.make_workload(name)
+    print("full size every token", name, add_inputs, NTHREADS, flush=True)
+    st = H.run_and_check(wl, add_inputs=add_inputs, prep=True, nthreads=NTHREADS)
     print(st, flush=True)
 
 
@@ -517,7 +538,8 @@ def test_fused_repeated_calls_and_no_lora():
             wl.mapping.copy_(mt)
             L = wl.layers[0]
             D = H.DevLayer(L)
-            buf = torch.zeros((3, m.size, 16), dtype=torch.float32, device="cuda")
+            # a fresh buffer each call: whatever it holds on entry is overwritten
+            buf = torch.full((3, m.size, 16), float(layer) - 7.5, dtype=torch.float32, device="cuda")
             y = D.y0.clone()
             sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, L.spec.scale)
             torch.cuda.synchronize()
@@ -525,7 +547,9 @@ def test_fused_repeated_calls_and_no_lora():
             tokens = np.arange(m.size, dtype=np.int32)
             buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
             buf_g, y_g = buf.cpu().numpy(), H.bits(y)
-            H.shrink_check(buf_g, buf_ref, bound)
+            act = m != -1
+            H.shrink_check(buf_g[:, act], buf_ref[:, act], bound[:, act])
+            assert np.all(buf_g[:, ~act] == np.float32(layer - 7.5)), "a -1 row of buf was touched"
             H.expand_check(y_g, y_ref, workloads.bf16_bits(L.y0), mag, True, H.propagated(L, m, buf_ref, bound))
 
 
@@ -564,7 +588,7 @@ def test_fused_graph_replay():
         if rep == 3:
             m[:] = -1
         mapping_dev.copy_(torch.from_numpy(m))
-        buf.zero_()
+        buf.fill_(rep + 0.25)   # a fresh buffer per call: its entry contents do not matter
         y.copy_(D.y0)
         torch.cuda.synchronize()
         print("fused graph replay", rep, flush=True)
@@ -574,7 +598,9 @@ def test_fused_graph_replay():
         H.check_sync_clear(meta, n)
         buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
         buf_g, y_g = buf.cpu().numpy(), H.bits(y)
-        H.shrink_check(buf_g, buf_ref, bound)
+        act = m != -1
+        assert np.all(buf_g[:, ~act] == np.float32(rep + 0.25))
+        H.shrink_check(buf_g[:, act], buf_ref[:, act], bound[:, act])
         H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
 
 
@@ -762,7 +788,7 @@ def test_prepare_fused_graph_replay():
         if rep == 1:
             m[:] = -1
         mapping_dev.copy_(torch.from_numpy(m))
-        buf.zero_()
+        buf.fill_(-rep - 0.5)   # a fresh buffer per call: its entry contents do not matter
         y.copy_(D.y0)
         H.poison_meta(meta)
         torch.cuda.synchronize()
@@ -774,7 +800,9 @@ def test_prepare_fused_graph_replay():
         assert int(host_flag[0]) == (1 if rep == 1 else 0)
         buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
         buf_g, y_g = buf.cpu().numpy(), H.bits(y)
-        H.shrink_check(buf_g, buf_ref, bound)
+        act = m != -1
+        assert np.all(buf_g[:, ~act] == np.float32(-rep - 0.5))
+        H.shrink_check(buf_g[:, act], buf_ref[:, act], bound[:, act])
         H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
     meta.struct.host_no_lora = None
 
@@ -804,15 +832,17 @@ def _kernel_nodes(graph) -> int:
     return sum(1 for k in kinds if k == 0)   # hipGraphNodeTypeKernel
 
 
-@pytest.mark.parametrize("name,n", [("decode", None), ("tiny", None), ("zipf", 1000), ("zipf", 3000),
-                                    ("prefill", 600), ("large", 300)])
+@pytest.mark.parametrize("name,n,layer", [("decode", None, 0), ("tiny", None, 0), ("zipf", 1000, 0),
+                                          ("zipf", 3000, 0), ("zipf", None, 1), ("prefill", 600, 0),
+                                          ("large", 300, 0)])
 @pytest.mark.parametrize("prep", [True, False])
-def test_launch_count_query_matches_the_calls(name, n, prep):
+def test_launch_count_query_matches_the_calls(name, n, layer, prep):
     """lora_shrink_expand_launches against the kernels a captured call really
-    launches: one inside the one-launch range, else the separate calls."""
+    launches: one inside the one-launch range, else the separate calls (with
+    the zeroing of buf's active rows before a split-K shrink)."""
     sgl = H.lib()
     wl = workloads.make_workload(name, num_tokens=n)
-    L = wl.layers[0]
+    L = wl.layers[layer]
     D = H.DevLayer(L)
     ntok = wl.mapping.numel()
     mapping = wl.mapping.to("cuda")
@@ -833,7 +863,8 @@ def test_launch_count_query_matches_the_calls(name, n, prep):
         else:
             sgl.lora_shrink_expand(D.x, D.a, D.b, D.bias, buf, y, meta, L.spec.scale)
     torch.cuda.current_stream().wait_stream(s)
-    want = sgl.lora_shrink_expand_launches(ntok, wl.spec.max_loras, len(L.spec.slices), L.spec.rank, prep)
+    want = sgl.lora_shrink_expand_launches(ntok, wl.spec.max_loras, L.spec.hidden, len(L.spec.slices),
+                                           L.spec.rank, prep)
     got = _kernel_nodes(g)
     print("launches", name, n, prep, want, got, flush=True)
     assert got == want
