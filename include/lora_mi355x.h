@@ -46,7 +46,8 @@ typedef enum lora_status {
     LORA_ERR_SLICES = -7,        /* num_slices outside [1, LORA_MAX_SLICES] */
     LORA_ERR_LAUNCH = -8,        /* the HIP runtime rejected a kernel launch or copy */
     LORA_ERR_ID_RANGE = -9,      /* device-side only: written to meta->status by prepare */
-    LORA_ERR_SYNC = -10          /* device-side only: a lora_shrink_expand wait timed out (meta->status) */
+    LORA_ERR_SYNC = -10,         /* device-side only: a lora_shrink_expand wait timed out (meta->status) */
+    LORA_ERR_SCRATCH = -11       /* lora_shrink_expand_noalloc: the buffer would exceed the library's array */
 } lora_status_t;
 
 #define LORA_MAX_LORAS 1023      /* ids 0 .. 1022; -1 = no LoRA */
@@ -241,6 +242,26 @@ int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const voi
                                const void *const *lora_a, const void *const *lora_b, const void *const *bias,
                                const int *slice_widths, int num_slices, int rank, float *buf, void *y,
                                int64_t ldy, int offset_start, int add_inputs, lora_meta_t *meta, float scale,
+                               hipStream_t stream);
+
+/*
+ * lora_shrink_expand for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors without `buf`; the fp32 buffer of
+ * the call lives in a device array of the library, 32 MiB (8388608 floats) per
+ * GPU, held by each GPU the library runs on until the process ends.  Calls
+ * needing num_slices * num_tokens * rank > 8388608 floats are rejected with
+ * LORA_ERR_SCRATCH before anything is launched.  Every call on one GPU uses
+ * that GPU's array (the device current at the call), so calls that overlap on
+ * one GPU -- on different streams, or from several threads -- race; calls
+ * ordered on one stream do not.  Nothing in the array needs clearing between
+ * calls (the buffer is written as a fresh one).  Allocates nothing: the array's
+ * address is looked up once per device on its first call.
+ */
+int lora_shrink_expand_noalloc(const void *x, int64_t ldx, int num_tokens, int hidden,
+                               const void *const *lora_a, const void *const *lora_b, const void *const *bias,
+                               const int *slice_widths, int num_slices, int rank, void *y, int64_t ldy,
+                               int offset_start, int add_inputs, const lora_meta_t *meta, float scale,
                                hipStream_t stream);
 
 /*

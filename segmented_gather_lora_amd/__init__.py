@@ -36,6 +36,7 @@ LORA_ERR_SLICES = -7
 LORA_ERR_LAUNCH = -8
 LORA_ERR_ID_RANGE = -9
 LORA_ERR_SYNC = -10
+LORA_ERR_SCRATCH = -11
 
 LORA_MAX_LORAS = 1023
 LORA_MAX_SLICES = 8
@@ -43,7 +44,7 @@ LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
             "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_shrink_expand_launches",
-            "lora_status_string", "lora_probe_read", "lora_probe_empty")
+            "lora_status_string", "lora_probe_read", "lora_probe_empty", "lora_shrink_expand_noalloc")
 
 
 class LoraError(RuntimeError):
@@ -90,6 +91,9 @@ def _load() -> ctypes.CDLL:
     lib.lora_shrink_expand.restype = i32
     lib.lora_shrink_expand.argtypes = [P, i64, i32, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
                                        ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
+    lib.lora_shrink_expand_noalloc.restype = i32
+    lib.lora_shrink_expand_noalloc.argtypes = [P, i64, i32, i32, P, P, P, P, i32, i32, P, i64, i32, i32,
+                                               ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
     lib.lora_prepare_shrink_expand.restype = i32
     lib.lora_prepare_shrink_expand.argtypes = [P, i32, P, i64, i32, P, P, P, P, i32, i32, P, P, i64, i32, i32,
                                                ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
@@ -351,6 +355,28 @@ def lora_shrink_expand(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Seq
                                   biasptrs, widths, s, r, buf.data_ptr(), y.data_ptr(), y.stride(0),
                                   int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
                                   float(scale), _stream(stream)), "lora_shrink_expand")
+
+
+def lora_shrink_expand_noalloc(x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], y,
+                               meta: LoraMeta, scale: float, offset_start: int = 0, add_inputs: bool = True,
+                               stream=None) -> None:
+    """lora_shrink_expand without a buffer argument, for callers that cannot
+    allocate: the fp32 buffer is the library's static device array (at most
+    8388608 floats, S * N * r; larger calls raise LORA_ERR_SCRATCH)."""
+    n, h = x.shape
+    r = lora_a[0].shape[1]
+    s = len(lora_a)
+    where = "lora_shrink_expand_noalloc"
+    _layer_checks(where, meta, n, x=x, lora_a=lora_a, lora_b=lora_b, bias=bias, y=y, offset_start=offset_start)
+    _need(len(lora_b) == s, LORA_ERR_SLICES, where, "one lora_b entry per lora_a entry")
+    _need(all(int(t.shape[2]) == r for t in lora_b) and all(int(t.shape[1]) == r for t in lora_a),
+          LORA_ERR_SHAPE, where, "lora_a and lora_b must share the rank")
+    widths = (ctypes.c_int * s)(*[int(t.shape[1]) for t in lora_b])
+    biasptrs = None if bias is None else _ptr_array(bias)
+    _check(_lib().lora_shrink_expand_noalloc(x.data_ptr(), x.stride(0), n, h, _ptr_array(lora_a),
+                                             _ptr_array(lora_b), biasptrs, widths, s, r, y.data_ptr(), y.stride(0),
+                                             int(offset_start), int(bool(add_inputs)), ctypes.byref(meta.struct),
+                                             float(scale), _stream(stream)), where)
 
 
 def lora_prepare_shrink_expand(mapping, x, lora_a: Sequence, lora_b: Sequence, bias: Optional[Sequence], buf, y,

@@ -422,6 +422,7 @@ const char *lora_status_string(int status) {
         case LORA_ERR_LAUNCH: return "HIP launch failed";
         case LORA_ERR_ID_RANGE: return "a LoRA id was outside [-1, max_loras) and was treated as -1";
         case LORA_ERR_SYNC: return "a fused shrink-expand wait on the device timed out";
+        case LORA_ERR_SCRATCH: return "the shrink buffer would exceed the library's static device array";
         default: return "unknown status";
     }
 }

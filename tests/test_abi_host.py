@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(sgl):
 
 
 def test_status_strings(sgl):
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         s = sgl.lora_status_string(code)
         assert s and s != "unknown status"
     assert sgl.lora_status_string(-100) == "unknown status"
