@@ -408,7 +408,10 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     layers_of = {"shrink": [i for i, L in enumerate(specs) if not L.expand_only],
                  "expand": list(range(len(specs))), "prepare": [0], "preplinear": [0], "copy": [0]}
     layers_of["linear"] = [i for i in layers_of["shrink"] if i > 0] or [0]
-    layers_of["zero"] = layers_of["shrink"]
+    # the zeroing of buf's rows runs only for layers whose call splits the shrink over K
+    wl = workloads.make_workload(workload)
+    layers_of["zero"] = [i for i in layers_of["shrink"]
+                         if launches(wl, i, i == 0) == (4 if i == 0 else 3)] or [0]
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
