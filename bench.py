@@ -395,6 +395,28 @@ def summarize_trace(trace_csv: str, plan_json: str, out_md: str, command: str) -
     return out
 
 
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    """Markdown table of a rocprofv3 --kernel-trace --stats summary
+    (kernel_stats.csv): calls and durations per kernel name, over the whole
+    run (every workload that launches the kernel)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "    " + command, "",
+             "kernel_hash: " + kernel_source_hash(), "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").replace("|", "/")
+        if name.endswith(")") and "(" in name:   # drop the parameter list
+            name = name[:name.rindex("(")]
+        lines.append("| %s | %s | %.3f | %.3f | %.3f | %.1f |" % (
+            name[:80], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, command: str) -> None:
     """Per-dispatch HBM traffic of each lora kernel from two rocprofv3 --pmc
     runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) of bench.py
@@ -751,6 +773,63 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     return rec
 
 
+def sweep(name: str, what: str, out_md: str, command: str) -> None:
+    """Time every tiling of one kernel on a full-size workload (the library's
+    tuning overrides; each changes the tiling only, never the result): the
+    LDS-staged shrink configurations x K splits, or the expand tile sizes x
+    column-block run lengths.  Cold inputs, HIP-graph replays of one call."""
+    import torch
+    import workloads
+    wl = workloads.make_workload(name)
+    sb = set_bytes(wl)
+    rotate = max(1, math.ceil((1 << 30) / sb)) if sb < LLC_BYTES else 1
+    first = DeviceSet(wl)
+    sets = [first] + [DeviceSet(wl, src=first) for _ in range(rotate - 1)]
+    for d in sets:
+        d.prepare()
+    torch.cuda.synchronize()
+    n = max(8, rotate)
+    env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_EXPAND_TILE_TOKENS",
+           "LORA_EXPAND_RUN")
+    if what == "shrink":
+        grid = [dict(LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
+                for c in range(1, 16) for k in (1, 2, 3, 4)]
+    else:
+        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
+                for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
+    grid.append({})   # the automatic choice
+    lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
+             "kernel_hash: " + kernel_source_hash(), "",
+             "us per launch (HIP events over graph replays, %d cold input set(s)); `auto` = the launcher's choice."
+             % rotate, ""]
+    for li, L in enumerate(wl.layers):
+        if what == "shrink" and L.spec.expand_only:
+            continue
+        res = []
+        for g in grid:
+            for k in env:
+                os.environ.pop(k, None)
+            os.environ.update(g)
+            fn = (lambda d: d.shrink(li)) if what == "shrink" else (lambda d: d.expand(li))
+            fn(sets[0])
+            torch.cuda.synchronize()
+            gr, seq = capture(lambda: [fn(sets[i % rotate]) for i in range(n)])
+            gr.replay()
+            us = time_graph(gr, seq, 3) / n * 1e3
+            label = " ".join("%s=%s" % (k[5:].lower(), v) for k, v in g.items() if k != "LORA_SHRINK_VARIANT") or "auto"
+            res.append((us, label))
+            print("# %s layer %d %s: %.2f us" % (what, li, label, us), file=sys.stderr, flush=True)
+        for k in env:
+            os.environ.pop(k, None)
+        res.sort()
+        auto = [u for u, lab in res if lab == "auto"][0]
+        lines += ["## layer %d (best %.2f us, auto %.2f us)" % (li, res[0][0], auto), "",
+                  "| tiling | us |", "|---|---|"] + ["| %s | %.2f |" % (lab, u) for u, lab in res] + [""]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -777,14 +856,21 @@ def main():
                     help="write the per-kernel traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_CSV", "PLAN_JSON", "OUT_MD", "COMMAND"),
                     help="write per-workload, per-layer kernel durations of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write the kernel statistics of one rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
                     help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
+    ap.add_argument("--sweep", nargs=3, metavar=("KERNEL", "OUT_MD", "COMMAND"),
+                    help="time every tiling of KERNEL (shrink or expand) on --workload and write a table")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
         return
     if args.summarize_mfma:
         summarize_mfma(args.workload, *args.summarize_mfma)
@@ -801,6 +887,9 @@ def main():
     import segmented_gather_lora_amd  # noqa: F401
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(args.workload, *args.sweep)
+        return
     if args.profile_steps:
         run_workload(args.workload, args, None, args.warmup, 0)
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
