@@ -667,20 +667,23 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     print("# %s: timed %d steps in %.4f s" % (name, steps, elapsed), file=sys.stderr, flush=True)
 
     # per-call average durations: graphs of >= 32 launches of one call kind
-    # cycling over the input sets
+    # cycling over the input sets; at least two sets, so that a call never
+    # finds the inputs of the launch before it in the last-level cache (a step
+    # streams the other calls' data in between)
     PLAN.phase = "per_call"
-    ncalls = max(32, rotate)
+    if rotate == 1 and not args.eager:
+        sets.append(DeviceSet(wl, src=first))
+    pc_rotate = len(sets)
+    ncalls = max(32, pc_rotate)
     reps = 2
 
     def per_call(fn):
-        g1, s1 = capture(lambda: [fn(sets[i % rotate]) for i in range(ncalls)])
+        g1, s1 = capture(lambda: [fn(sets[i % pc_rotate]) for i in range(ncalls)])
         g1.replay()
         PLAN.replay(s1, 1)
         return time_graph(g1, s1, reps) / ncalls
 
-    kern = {}
-    if not all(L.spec.expand_only for L in wl.layers) or True:
-        kern["prepare"] = per_call(lambda s: s.prepare())
+    kern = {"prepare": per_call(lambda s: s.prepare())}
     for li in range(nl):
         if not wl.layers[li].spec.expand_only:
             kern["shrink%d" % li] = per_call(lambda s: s.shrink(li))
@@ -727,7 +730,7 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
            "layers": [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
                        "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
                       for L in wl.layers],
-           "input_sets_rotated": rotate, "steps": steps, "ms_per_step": round(ms_per_step, 5),
+           "input_sets_rotated": rotate, "per_call_input_sets": pc_rotate, "steps": steps, "ms_per_step": round(ms_per_step, 5),
            "tokens_per_s": round(tokens_per_s, 1), "step_bytes": step_bytes,
            "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
            "step_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -790,13 +793,15 @@ def sweep(name: str, what: str, out_md: str, command: str) -> None:
     torch.cuda.synchronize()
     n = max(8, rotate)
     env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_EXPAND_TILE_TOKENS",
-           "LORA_EXPAND_RUN")
+           "LORA_EXPAND_RUN", "LORA_EXPAND_SUB")
     if what == "shrink":
         grid = [dict(LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
                 for c in range(1, 16) for k in (1, 2, 3, 4)]
     else:
-        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
+        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r), LORA_EXPAND_SUB="1")
                 for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
+        grid += [dict(LORA_EXPAND_TILE_TOKENS="64", LORA_EXPAND_RUN=str(r), LORA_EXPAND_SUB="2")
+                 for r in (1, 2, 4, 8, 16)]
     grid.append({})   # the automatic choice
     lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
              "kernel_hash: " + kernel_source_hash(), "",
