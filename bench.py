@@ -793,15 +793,13 @@ def sweep(name: str, what: str, out_md: str, command: str) -> None:
     torch.cuda.synchronize()
     n = max(8, rotate)
     env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_EXPAND_TILE_TOKENS",
-           "LORA_EXPAND_RUN", "LORA_EXPAND_SUB")
+           "LORA_EXPAND_RUN")
     if what == "shrink":
         grid = [dict(LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
                 for c in range(1, 16) for k in (1, 2, 3, 4)]
     else:
-        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r), LORA_EXPAND_SUB="1")
+        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
                 for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
-        grid += [dict(LORA_EXPAND_TILE_TOKENS="64", LORA_EXPAND_RUN=str(r), LORA_EXPAND_SUB="2")
-                 for r in (1, 2, 4, 8, 16)]
     grid.append({})   # the automatic choice
     lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
              "kernel_hash: " + kernel_source_hash(), "",

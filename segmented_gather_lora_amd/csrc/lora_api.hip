@@ -301,7 +301,6 @@ ExpandTuning expand_tuning() {
     if (cfg.tile_tokens % 16) cfg.tile_tokens = 0;
     cfg.grid_cap = env_int("LORA_EXPAND_GRID");
     cfg.run_blocks = env_int("LORA_EXPAND_RUN");
-    cfg.sub = env_int("LORA_EXPAND_SUB");
     return cfg;
 }
 

@@ -7,12 +7,9 @@
 // Per segment and slice this is C[tokens][cols] = buf_seg[tokens][r] * B_id[cols][r]^T
 // with K = r (8..128), on the bf16 MFMA (v_mfma_f32_16x16x32_bf16) with the
 // tokens on the M side and the output columns on the N side:
-//   - a work unit is (SUB sub-tiles of TT tiles of 16 tokens of one segment)
-//     x (a run of 256-column blocks of one slice); each of the 4 waves owns 64
-//     of a block's columns and keeps their weights (64 x r bf16) in registers
-//     for all the unit's sub-tiles, which it runs one after the other (with
-//     two 64-token sub-tiles, a segment of up to 128 tokens reads each block's
-//     weights once);
+//   - a work unit is (TT tiles of 16 tokens of one segment) x (256 columns of
+//     one slice); each of the 4 waves owns 64 of the columns and keeps their
+//     weights (64 x r bf16) in registers for the unit;
 //   - the unit's fp32 buffer rows are read once per workgroup with coalesced
 //     loads, split into bf16 hi = rne(v) and lo = rne(v - hi) and staged in
 //     LDS; every wave reads its MFMA operands from there, and both parts go
@@ -28,12 +25,11 @@
 // walked by a persistent grid.
 //
 // No load or store is conditional.  A lane whose token is past the end of
-// the segment works on the last token of its sub-tile's part of the segment,
-// and a 4-column group past the end of the slice works on the slice's last 4
-// columns: it computes exactly the owner's values (from the same y, loaded
-// before any store of the sub-tile) and stores them to the same address, so
-// the duplicate store is harmless; a sub-tile wholly past the segment is
-// skipped.  Tokens with id -1 own no tile and are never touched.
+// the segment works on the segment's last token, and a 4-column group past
+// the end of the slice works on the slice's last 4 columns: it computes
+// exactly the owner's values and stores them to the same address, so the
+// duplicate store is harmless.  Tokens with id -1 own no tile and are never
+// touched.
 #include "lora_internal.h"
 
 namespace lora {
@@ -61,28 +57,16 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return
 // Last valid 4-column group for a group starting at c (c % 4 == 0).
 __device__ __forceinline__ int clamp_group(int c, int width) { return c < width ? c : width - 4; }
 
-// KS: 32-wide K steps (rank <= 32*KS); TT: 16-token tiles per sub-tile (their
-// y rows are held in registers together); SUB: sub-tiles per unit, which share
-// each column block's weights (loaded once per block for all SUB*16*TT tokens
-// of the unit, so a segment of up to that many tokens reads its weights once).
-// Units of two sub-tiles hold two workgroups per CU by LDS; their registers
-// are held to two waves per SIMD as well.
-template <int SUB>
-constexpr int kExpandWavesPerSimd = SUB > 1 ? 2 : 1;
-
-template <int KS, int TT, int SUB, bool ADD, bool EARLY>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kExpandWavesPerSimd<SUB>)))
-void expand_kernel(ExpandArgs a) {
+template <int KS, int TT, bool ADD, bool EARLY>
+__global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     prefetch_kernargs<ExpandArgs>();
-    constexpr int kSubTokens = 16 * TT;
-    constexpr int kUnitTokens = kSubTokens * SUB;
+    constexpr int kUnitTokens = 16 * TT;
     constexpr int kRowK = 32 * KS;              // bf16 per staged row (rank padded to 32)
     constexpr int kRowStride = kRowK + 8;       // +16 bytes: rows start on different banks
     extern __shared__ int smem[];
     __shared__ int s_wsum[kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t s_hi[kUnitTokens * kRowStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_lo[kUnitTokens * kRowStride];
-    __shared__ int s_tok[SUB > 1 ? kUnitTokens : 1];   // token of each unit row (sub-tiles after the first)
 
     const int nslots = a.meta.nslots;
     const int total = build_tile_table<kThreads>(a.meta, kUnitTokens, smem, s_wsum);
@@ -116,7 +100,7 @@ void expand_kernel(ExpandArgs a) {
         constexpr int kMinRowsPerPass = kThreads / (8 * KS);
         constexpr int kPasses = (kUnitTokens + kMinRowsPerPass - 1) / kMinRowsPerPass;
         floatx4 bvals[kPasses];
-        int brow_p[kPasses], brow_t[kPasses];
+        int brow_p[kPasses];
 #pragma unroll
         for (int ps = 0; ps < kPasses; ++ps) {
             int p = ps * rows_per_pass + tid / lanes_per_row;
@@ -127,10 +111,9 @@ void expand_kernel(ExpandArgs a) {
             pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
             int t = sorted_at(a.meta, smem, tr.seg_start + pp);
             t = (unsigned)t < (unsigned)a.num_tokens ? t : a.num_tokens - 1;
-            brow_t[ps] = t;
             bvals[ps] = *reinterpret_cast<const floatx4 *>(bufs + (int64_t)t * rank + 4 * piece);
         }
-        // ---- y rows of the first sub-tile: tile q, row 4g + e of the tile -> token index
+        // ---- y rows of this lane: tile q, row 4g + e of the tile -> token index
         int ytok[TT][4];
 #pragma unroll
         for (int q = 0; q < TT; ++q)
@@ -144,9 +127,9 @@ void expand_kernel(ExpandArgs a) {
 
         // ---- operands of one column block for this wave: weights (B operand of
         // n-tile q: lane (n16, g) -> column 4*n16 + q), bias and y rows.  With
-        // EARLY (runs of one block) the first block's are loaded before the
-        // buffer rows are staged, in the same round trip; longer runs load them
-        // block by block (fewer registers live across the staging).
+        // EARLY (runs of one block) they are loaded before the buffer rows are
+        // staged, in the same round trip; longer runs load them block by block
+        // (fewer registers live across the staging).
         const uint16_t *wslice = select_slice(a.b, i) + (int64_t)tr.lora_id * width * rank;
         const uint16_t *bptr = select_slice(a.bias, i);
         const int slice_col = select_slice(a.col_off, i);
@@ -159,7 +142,7 @@ void expand_kernel(ExpandArgs a) {
             asm volatile("" : "+v"(row));
             return a.y + ((int64_t)row * a.ldy + col);
         };
-        auto load_weights = [&](int grp) {
+        auto load_block = [&](int grp) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint16_t *row = wslice + (int64_t)(grp + q) * rank;
@@ -170,8 +153,6 @@ void expand_kernel(ExpandArgs a) {
                 }
             }
             braw = bptr ? *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp) : u32x2{0u, 0u};
-        };
-        auto load_y = [&](int grp) {
             const int ycol = slice_col + grp;
 #pragma unroll
             for (int q = 0; q < TT; ++q)
@@ -180,21 +161,11 @@ void expand_kernel(ExpandArgs a) {
                     yv[q][e] = ADD ? __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(y_at(ytok[q][e], ycol)))
                                    : u32x2{0u, 0u};
         };
-        // token rows of sub-tile sb (sb >= 1) from the staged list
-        auto sub_tokens = [&](int sb) {
-#pragma unroll
-            for (int q = 0; q < TT; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ytok[q][e] = s_tok[sb * kSubTokens + q * 16 + 4 * g + e];
-        };
         // first of this lane's 4 columns in block cb0 + c (clamped to the slice)
         auto group_of = [&](int c) {
             return clamp_group((cb0 + c) * kBlockCols + wave * kWaveCols + 4 * n16, width);
         };
-        if (EARLY) {
-            load_weights(group_of(0));
-            load_y(group_of(0));
-        }
+        if (EARLY) load_block(group_of(0));
 
         // ---- stage the buffer rows in LDS as bf16 hi / lo (rank tail stays zero),
         // once for all column blocks of the run
@@ -211,7 +182,6 @@ void expand_kernel(ExpandArgs a) {
                 }
                 *reinterpret_cast<u32x2 *>(&s_hi[p * kRowStride + 4 * piece]) = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
                 *reinterpret_cast<u32x2 *>(&s_lo[p * kRowStride + 4 * piece]) = u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])};
-                if (SUB > 1 && piece == 0) s_tok[p] = brow_t[ps];
             }
         }
         if (rank < kRowK) {   // zero the rank padding once per unit
@@ -227,7 +197,7 @@ void expand_kernel(ExpandArgs a) {
             // a wave past the slice's last column stays past it for the rest of the run
             if ((cb0 + c) * kBlockCols + wave * kWaveCols >= width) break;
             const int grp = group_of(c);
-            if (!EARLY || c > 0) load_weights(grp);
+            if (!EARLY || c > 0) load_block(grp);
 
             // K positions >= rank: zero the weights (no NaN from stale data)
 #pragma unroll
@@ -243,46 +213,33 @@ void expand_kernel(ExpandArgs a) {
             bias[3] = bf16_bits_to_float(braw[1] >> 16);
             const int ycol = slice_col + grp;
 
-            // sub-tiles one after the other (not unrolled: the second sub-tile's y
-            // loads must not be hoisted above the first one's stores, which would
-            // hold two sets of y registers).  A sub-tile wholly past the
-            // segment's end is skipped: its rows would repeat the segment's last
-            // token, whose y the first sub-tile has already updated.  A partly
-            // filled one repeats a token of its own, loaded before any store.
-            const int nsub = (SUB > 1 && pbase + kSubTokens < tr.seg_count) ? SUB : 1;
-#pragma unroll 1
-            for (int sb = 0; sb < nsub; ++sb) {
-                if (sb > 0) sub_tokens(sb);
-                else if (SUB > 1 && c > 0) sub_tokens(0);
-                if (!EARLY || c > 0 || sb > 0) load_y(grp);
 #pragma unroll
-                for (int q = 0; q < TT; ++q) {
-                    floatx4 acc[4];
+            for (int q = 0; q < TT; ++q) {
+                floatx4 acc[4];
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4) acc[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int t4 = 0; t4 < 4; ++t4) acc[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int off = (sb * kSubTokens + q * 16 + n16) * kRowStride + ks * 32 + 8 * g;
-                        const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_hi[off]);
-                        const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lo[off]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int off = (q * 16 + n16) * kRowStride + ks * 32 + 8 * g;
+                    const u32x4 ah = *reinterpret_cast<const u32x4 *>(&s_hi[off]);
+                    const u32x4 al = *reinterpret_cast<const u32x4 *>(&s_lo[off]);
 #pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4) {
-                            acc[t4] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(w[t4][ks]), acc[t4]);
-                            acc[t4] = mfma16x16x32(as_bf16x8(al), as_bf16x8(w[t4][ks]), acc[t4]);
-                        }
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        acc[t4] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(w[t4][ks]), acc[t4]);
+                        acc[t4] = mfma16x16x32(as_bf16x8(al), as_bf16x8(w[t4][ks]), acc[t4]);
                     }
-                    // acc[t4][e]: token row 4g + e of tile q, column grp + t4
+                }
+                // acc[t4][e]: token row 4g + e of tile q, column grp + t4
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const u32x2 yy = yv[q][e];
-                        const float r0 = bf16_bits_to_float(yy[0] & 0xffffu) + (acc[0][e] + bias[0]);
-                        const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][e] + bias[1]);
-                        const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][e] + bias[2]);
-                        const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][e] + bias[3]);
-                        __builtin_nontemporal_store(u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
-                                                          pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))},
-                                                    reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)));
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const u32x2 yy = yv[q][e];
+                    const float r0 = bf16_bits_to_float(yy[0] & 0xffffu) + (acc[0][e] + bias[0]);
+                    const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][e] + bias[1]);
+                    const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][e] + bias[2]);
+                    const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][e] + bias[3]);
+                    __builtin_nontemporal_store(u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                                                      pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))},
+                                                reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)));
                 }
             }
         }
@@ -292,28 +249,27 @@ void expand_kernel(ExpandArgs a) {
 
 typedef void (*ExpandFn)(ExpandArgs);
 
-template <int KS, int TT, int SUB>
+template <int KS, int TT>
 ExpandFn pick_add(bool add, bool early) {
-    if (early) return add ? expand_kernel<KS, TT, SUB, true, true> : expand_kernel<KS, TT, SUB, false, true>;
-    return add ? expand_kernel<KS, TT, SUB, true, false> : expand_kernel<KS, TT, SUB, false, false>;
+    if (early) return add ? expand_kernel<KS, TT, true, true> : expand_kernel<KS, TT, false, true>;
+    return add ? expand_kernel<KS, TT, true, false> : expand_kernel<KS, TT, false, false>;
 }
 
 template <int KS>
-ExpandFn pick_tt(int tt, int sub, bool add, bool early) {
-    if (sub > 1) return pick_add<KS, 4, 2>(add, early);   // two 64-token sub-tiles
+ExpandFn pick_tt(int tt, bool add, bool early) {
     switch (tt) {
-        case 1: return pick_add<KS, 1, 1>(add, early);
-        case 2: return pick_add<KS, 2, 1>(add, early);
-        default: return pick_add<KS, 4, 1>(add, early);
+        case 1: return pick_add<KS, 1>(add, early);
+        case 2: return pick_add<KS, 2>(add, early);
+        default: return pick_add<KS, 4>(add, early);
     }
 }
 
-ExpandFn pick(int ks, int tt, int sub, bool add, bool early) {
+ExpandFn pick(int ks, int tt, bool add, bool early) {
     switch (ks) {
-        case 1: return pick_tt<1>(tt, sub, add, early);
-        case 2: return pick_tt<2>(tt, sub, add, early);
-        case 3: return pick_tt<3>(tt, sub, add, early);
-        default: return pick_tt<4>(tt, sub, add, early);
+        case 1: return pick_tt<1>(tt, add, early);
+        case 2: return pick_tt<2>(tt, add, early);
+        case 3: return pick_tt<3>(tt, add, early);
+        default: return pick_tt<4>(tt, add, early);
     }
 }
 
@@ -342,15 +298,7 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
         if (a.rank <= 32 && tt > 2) tt = 2;
     }
     tt = tt >= 4 ? 4 : (tt >= 2 ? 2 : 1);
-    // Two 64-token sub-tiles per unit, which share each block's weights, when
-    // segments are longer than one 64-token tile (the weights of a segment's
-    // column block are then read once per 128 tokens instead of once per 64).
-    int sub = cfg.sub > 0 ? cfg.sub : ((tt == 4 && a.rank > 32 && avg > 64) ? 2 : 1);
-    if (sub > 1) {
-        sub = 2;
-        tt = 4;
-    }
-    a.tile_tokens = 16 * tt * sub;
+    a.tile_tokens = 16 * tt;
     const bool add = a.add_inputs != 0;
     a.meta.lds_tokens = n <= kLdsTokensMax ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
@@ -380,7 +328,7 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
     }
     a.run_blocks = r;
     a.runs = (int)count_runs(r);
-    const ExpandFn fn = pick(ks, tt, sub, add, r == 1);
+    const ExpandFn fn = pick(ks, tt, add, r == 1);
     const long units_upper = tiles_upper * a.runs;
     a.num_units = (int)units_upper;
     const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : 2048,

@@ -369,7 +369,6 @@ struct ExpandTuning {
     int tile_tokens;       // 16, 32 or 64
     int grid_cap;
     int run_blocks;        // column blocks per unit
-    int sub;               // 1 or 2 sub-tiles of 64 tokens per unit
 };
 
 // Workgroups of kernel `fn` the device holds at once (host side, cached).

@@ -251,21 +251,6 @@ def test_expand_run_variants(run, tt, rank, add_inputs, monkeypatch):
     H.run_and_check(wl, add_inputs=add_inputs, offset_start=16, ldy_extra=8)
 
 
-@pytest.mark.parametrize("run", [1, 2, 3, 8])
-@pytest.mark.parametrize("name,n", [("prefill", 700), ("large", 300), ("decode", None)])
-@pytest.mark.parametrize("add_inputs", [True, False])
-def test_expand_two_sub_tiles(name, n, run, add_inputs, monkeypatch):
-    """Units of two 64-token sub-tiles sharing each column block's weights
-    (ranks 16, 64, 128), with runs of 1 (the early-load form), 2, 3 and 8
-    column blocks; every token."""
-    monkeypatch.setenv("LORA_EXPAND_SUB", "2")
-    monkeypatch.setenv("LORA_EXPAND_RUN", str(run))
-    wl = workloads.make_workload(name, num_tokens=n)
-    print("expand two sub-tiles", name, n, run, add_inputs, flush=True)
-    H.run_and_check(wl, add_inputs=add_inputs)
-    print(H.run_expand_only(wl, add_inputs), flush=True)
-
-
 def _gpu_outputs(wl, meta, buf0=None):
     sgl = H.lib()
     L = wl.layers[0]
