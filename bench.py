@@ -35,6 +35,7 @@ import hashlib
 import json
 import math
 import os
+import shlex
 import sys
 import time
 
@@ -776,7 +777,7 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     return rec
 
 
-def sweep(name: str, what: str, out_md: str, command: str) -> None:
+def sweep(name: str, what: str, out_md: str) -> None:
     """Time every tiling of one kernel on a full-size workload (the library's
     tuning overrides; each changes the tiling only, never the result): the
     LDS-staged shrink configurations x K splits, or the expand tile sizes x
@@ -801,6 +802,7 @@ def sweep(name: str, what: str, out_md: str, command: str) -> None:
         grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
                 for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
     grid.append({})   # the automatic choice
+    command = "python bench.py " + " ".join(shlex.quote(a) for a in sys.argv[1:])
     lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
              "kernel_hash: " + kernel_source_hash(), "",
              "us per launch (HIP events over graph replays, %d cold input set(s)); `auto` = the launcher's choice."
@@ -863,7 +865,7 @@ def main():
                     help="write the kernel statistics of one rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
                     help="write the per-kernel MFMA use of one rocprofv3 --pmc run and exit")
-    ap.add_argument("--sweep", nargs=3, metavar=("KERNEL", "OUT_MD", "COMMAND"),
+    ap.add_argument("--sweep", nargs=2, metavar=("KERNEL", "OUT_MD"),
                     help="time every tiling of KERNEL (shrink or expand) on --workload and write a table")
     args = ap.parse_args()
     if args.summarize_pmc:
