@@ -777,14 +777,15 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     return rec
 
 
-def sweep(name: str, what: str, out_md: str) -> None:
+def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     """Time every tiling of one kernel on a full-size workload (the library's
     tuning overrides; each changes the tiling only, never the result): the
     LDS-staged shrink configurations x K splits, or the expand tile sizes x
     column-block run lengths.  Cold inputs, HIP-graph replays of one call."""
     import torch
     import workloads
-    wl = workloads.make_workload(name)
+    if wl is None:
+        wl = workloads.make_workload(name)
     sb = set_bytes(wl)
     rotate = max(1, math.ceil((1 << 30) / sb)) if sb < LLC_BYTES else 1
     first = DeviceSet(wl)
@@ -793,15 +794,18 @@ def sweep(name: str, what: str, out_md: str) -> None:
         d.prepare()
     torch.cuda.synchronize()
     n = max(8, rotate)
-    env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_EXPAND_TILE_TOKENS",
-           "LORA_EXPAND_RUN")
-    if what == "shrink":
+    env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_SHRINK_SK",
+           "LORA_EXPAND_TILE_TOKENS", "LORA_EXPAND_RUN")
+    if grid is not None:
+        grid = [dict(g) for g in grid]
+    elif what == "shrink":
         grid = [dict(LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
-                for c in range(1, 16) for k in (1, 2, 3, 4)]
+                for c in range(1, 20) for k in (1, 2, 3, 4)]
     else:
         grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
                 for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
-    grid.append({})   # the automatic choice
+    if {} not in grid:
+        grid.append({})   # the automatic choice
     command = "python bench.py " + " ".join(shlex.quote(a) for a in sys.argv[1:])
     lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
              "kernel_hash: " + kernel_source_hash(), "",

@@ -46,7 +46,7 @@ typedef enum lora_status {
     LORA_ERR_SLICES = -7,        /* num_slices outside [1, LORA_MAX_SLICES] */
     LORA_ERR_LAUNCH = -8,        /* the HIP runtime rejected a kernel launch or copy */
     LORA_ERR_ID_RANGE = -9,      /* device-side only: written to meta->status by prepare */
-    LORA_ERR_SYNC = -10,         /* device-side only: a lora_shrink_expand wait timed out (meta->status) */
+    LORA_ERR_SYNC = -10,         /* device-side only: a device wait of a shrink timed out (meta->status) */
     LORA_ERR_SCRATCH = -11       /* lora_shrink_expand_noalloc: the buffer would exceed the library's array */
 } lora_status_t;
 
@@ -71,8 +71,10 @@ typedef enum lora_status {
  *   sync                   int32[128 * (ceil(T / 16) + min(max_loras + 1, T) + 1)]
  *                          followed by float32[64 * T] and float32[1024 * min(T, 2048)],
  *                          T = min(max_num_tokens, 24576): counters, accumulation
- *                                     area and part slots of the one-launch calls
- *                                     (library-owned)
+ *                                     area and part slots of the one-launch calls;
+ *                          then, when max_num_tokens >= 1024, int32[1024] and
+ *                          float32[8 << 20]: counters and part slots of the
+ *                          stream-K shrink (library-owned)
  * The struct itself lives in host memory; lora_prepare_meta() records
  * num_tokens in it.
  */
@@ -85,10 +87,10 @@ typedef struct lora_meta {
     int32_t *no_lora_flag;
     int32_t *status;
     int32_t *sync;           /* work counters, fp32 accumulation area and part slots of the
-                                one-launch calls (library-owned part of the region): the
-                                counters and the accumulation area are zeroed by
-                                lora_prepare_meta for batches those calls can take and left
-                                zero by every such call that completes without
+                                one-launch calls and of the stream-K shrink (library-owned
+                                part of the region): the counters and the accumulation area
+                                are zeroed by lora_prepare_meta for batches that can use
+                                them and left zero by every call that completes without
                                 LORA_ERR_SYNC; the part slots need no clearing */
     int32_t *host_no_lora;   /* optional host pinned word (NULL = none): prepare copies
                                 no_lora_flag into it asynchronously on its stream */
@@ -138,8 +140,19 @@ int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta,
  *   buf     float32 [num_slices][num_tokens][rank], 16-byte aligned
  *   hidden % 8 == 0, rank % 8 == 0, 8 <= rank <= LORA_MAX_RANK
  * num_tokens must equal the N of the last lora_prepare_meta() on `meta`,
- * whose results must be complete in stream order.  Split-K partial sums are
- * combined with float atomics, so the last bits may vary between runs.
+ * whose results must be complete in stream order.
+ * Batches of at least 1024 tokens whose segments are long enough for the
+ * LDS-staged kernel may be split by K steps over the workgroups (stream-K):
+ * the workgroups that start a tile in the middle store their partial sums
+ * in part slots of meta->sync and count them, and the workgroup holding the
+ * tile's first K steps waits on the device for that count, adds the slots
+ * in order and writes buf (deterministic).  Calls sharing one metadata
+ * region must then not overlap (on one stream they never do).  A wait that
+ * never ends (not expected: the parts it waits for start before anything
+ * that waits) gives up after about 0.1 s and sets meta->status to
+ * LORA_ERR_SYNC; buf and the stream-K counters are then unspecified, and a
+ * lora_prepare_meta must run before the next call.  Other shapes may split
+ * K with float atomics into buf, whose last bits may then vary between runs.
  */
 int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden,
                 const void *const *lora_a, int num_slices, int rank,
@@ -197,8 +210,9 @@ int lora_expand(const float *buf, int num_tokens, int rank,
  * prepared id copy (token_lora_mapping) rather than the sorted indices; its
  * parts store their sums in part slots of meta->sync and the expand adds them
  * up in part order, so buf is deterministic in that layout.
- * Other shapes launch the separate kernels (a split-K shrink also zeroes the
- * active rows of buf first).  The one-launch kernels use meta->sync: calls
+ * Other shapes launch the separate kernels (lora_shrink with buf written, not
+ * accumulated, then lora_expand; a shrink split over K with float atomics
+ * zeroes the active rows of buf first).  The one-launch kernels use meta->sync: calls
  * sharing one metadata region must not overlap (they are ordered on one
  * stream in normal use), and meta must have been prepared at least once since
  * it was bound; every call that completes normally leaves the counters and
@@ -207,8 +221,8 @@ int lora_expand(const float *buf, int num_tokens, int rank,
  * running workgroup) gives up after about 0.1 s and sets meta->status to
  * LORA_ERR_SYNC.  After that, y, buf and the counters and accumulation area
  * of meta->sync are unspecified: the call's results must be discarded, and
- * a lora_prepare_meta of a batch the one-launch calls can take must run
- * before the next one-launch call (it clears the counters and the area).
+ * a lora_prepare_meta must run before the next call (it clears the counters
+ * and the area).  The same holds for the stream-K shrink's wait.
  */
 int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden,
                        const void *const *lora_a, const void *const *lora_b, const void *const *bias,

@@ -105,7 +105,7 @@ size_t lora_meta_bytes(int max_loras, int max_num_tokens) {
     const size_t tok = round_up(sizeof(int32_t) * (size_t)(max_num_tokens > 0 ? max_num_tokens : 1));
     return 2 * tok + 2 * round_up(sizeof(int32_t) * (max_loras + 1)) +
            round_up(sizeof(int32_t) * (max_loras + 2)) + 2 * kAlign +
-           round_up(sizeof(int32_t) * (size_t)fused_region_words(max_num_tokens, max_loras + 1));
+           round_up(sizeof(int32_t) * (size_t)meta_region_words(max_num_tokens, max_loras + 1));
 }
 
 int lora_meta_bind(void *dev, size_t bytes, int max_loras, int max_num_tokens, lora_meta_t *out) {
@@ -155,6 +155,17 @@ float *fused_slots(const lora_meta_t *meta) {
     return reinterpret_cast<float *>(meta->sync + fused_sync_words(meta->max_num_tokens, meta->max_loras + 1));
 }
 
+// The stream-K shrink's counters and slots, after the part slots (nullptr
+// when the region was bound for fewer than kSkMinTokens tokens).
+int32_t *sk_counters(const lora_meta_t *meta) {
+    if (sk_region_words(meta->max_num_tokens) == 0) return nullptr;
+    return meta->sync + fused_region_words(meta->max_num_tokens, meta->max_loras + 1);
+}
+float *sk_slots(const lora_meta_t *meta) {
+    int32_t *c = sk_counters(meta);
+    return c ? reinterpret_cast<float *>(c + kSkCounterWords) : nullptr;
+}
+
 PrepareArgs prepare_args(const int32_t *mapping, int num_tokens, const lora_meta_t *meta) {
     PrepareArgs a;
     a.mapping = mapping;
@@ -193,7 +204,11 @@ int lora_prepare_meta(const int32_t *mapping, int num_tokens, lora_meta_t *meta,
     if (st) return st;
     if (num_tokens < 0 || num_tokens > meta->max_num_tokens) return LORA_ERR_NUM_TOKENS;
     if (num_tokens > 0 && !mapping) return LORA_ERR_NULL;
-    if (launch_prepare(prepare_args(mapping, num_tokens, meta), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    // the stream-K shrink's counters start every batch that may use it at zero
+    int32_t *skc = sk_counters(meta);
+    const int sk_words = skc && num_tokens >= kSkMinTokens ? kSkCounterWords : 0;
+    if (launch_prepare(prepare_args(mapping, num_tokens, meta), skc, sk_words, stream) != hipSuccess)
+        return LORA_ERR_LAUNCH;
     if ((st = mirror_flag(meta, stream))) return st;
     meta->num_tokens = num_tokens;
     return LORA_OK;
@@ -238,6 +253,14 @@ int shrink_args(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     return LORA_OK;
 }
 
+SkArgs sk_args(const lora_meta_t *meta) {
+    SkArgs k;
+    k.slots = sk_slots(meta);
+    k.counters = sk_counters(meta);
+    k.status = meta->status;
+    return k;
+}
+
 ShrinkTuning shrink_tuning() {
     ShrinkTuning cfg;
     cfg.tile_tokens = env_int("LORA_SHRINK_TILE_TOKENS");
@@ -247,6 +270,7 @@ ShrinkTuning shrink_tuning() {
     cfg.grid_cap = env_int("LORA_SHRINK_GRID");
     cfg.variant = env_int("LORA_SHRINK_VARIANT");
     cfg.staged_cfg = env_int("LORA_SHRINK_STAGED");
+    cfg.stream_k = env_int("LORA_SHRINK_SK");
     return cfg;
 }
 
@@ -315,7 +339,7 @@ int lora_shrink(const void *x, int64_t ldx, int num_tokens, int hidden, const vo
     bool skip = false;
     const int st = shrink_args(x, ldx, num_tokens, hidden, lora_a, num_slices, rank, buf, meta, scale, a, skip);
     if (st || skip) return st;
-    if (launch_shrink(a, shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    if (launch_shrink(a, sk_args(meta), shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }
 
@@ -355,7 +379,7 @@ int lora_shrink_expand(const void *x, int64_t ldx, int num_tokens, int hidden, c
         if (e == hipSuccess) return LORA_OK;
         if (e != hipErrorNotSupported) return LORA_ERR_LAUNCH;
     }
-    if (launch_shrink(sa, shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
+    if (launch_shrink(sa, sk_args(meta), shrink_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     if (launch_expand(ea, expand_tuning(), stream) != hipSuccess) return LORA_ERR_LAUNCH;
     return LORA_OK;
 }
@@ -421,7 +445,7 @@ const char *lora_status_string(int status) {
         case LORA_ERR_SLICES: return "num_slices out of range";
         case LORA_ERR_LAUNCH: return "HIP launch failed";
         case LORA_ERR_ID_RANGE: return "a LoRA id was outside [-1, max_loras) and was treated as -1";
-        case LORA_ERR_SYNC: return "a fused shrink-expand wait on the device timed out";
+        case LORA_ERR_SYNC: return "a shrink's wait on the device timed out";
         case LORA_ERR_SCRATCH: return "the shrink buffer would exceed the library's static device array";
         default: return "unknown status";
     }

@@ -334,6 +334,15 @@ struct ShrinkArgs {
     float scale;
 };
 
+// The stream-K shrink's extra arguments: part slots and counters in the
+// library-owned area (nullptr when the area has none), and the status word
+// for a wait that times out.
+struct SkArgs {
+    float *slots;
+    int32_t *counters;
+    int32_t *status;
+};
+
 struct ExpandArgs {
     MetaView meta;
     const float *buf;
@@ -364,6 +373,7 @@ struct ShrinkTuning {
     int grid_cap;
     int variant;           // 2 = direct-load kernel, 3 = LDS-staged kernel
     int staged_cfg;        // 1-based index into the LDS-staged configurations
+    int stream_k;          // 0 automatic, 1 never, 2 whenever the batch allows it
 };
 struct ExpandTuning {
     int tile_tokens;       // 16, 32 or 64
@@ -384,8 +394,10 @@ inline long persistent_grid(long units, long cap, const void *fn, int threads, s
 }
 
 // Host-side launchers (defined next to their kernels).
-hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
-hipError_t launch_shrink(const ShrinkArgs &a, const ShrinkTuning &cfg, hipStream_t s);
+// Also zeroes the stream-K shrink's counters (sk_words words at sk_counters;
+// none when sk_words is 0).
+hipError_t launch_prepare(const PrepareArgs &a, int32_t *sk_counters, int sk_words, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs &a, const SkArgs &sk, const ShrinkTuning &cfg, hipStream_t s);
 // Kernel launches launch_shrink makes for these sizes (host only): 2 when a
 // fresh buffer (overwrite) is combined from K chunks and its rows are zeroed
 // first, else 1 (0 for an empty batch).
@@ -442,6 +454,22 @@ constexpr long kLmMaxTokens = 2048;
 inline long lm_slot_floats(long n) { return (long)kLmMaxParts * kFusedAccPerToken * (n < kLmMaxTokens ? n : kLmMaxTokens); }
 inline long fused_region_words(long max_num_tokens, long nslots) {
     return fused_sync_words(max_num_tokens, nslots) + lm_slot_floats(max_num_tokens);
+}
+// After the part slots, for regions bound for at least kSkMinTokens tokens,
+// the stream-K shrink's area: kSkCounterWords counters (one per share
+// boundary and row block, zeroed by prepare and left zero by every launch),
+// then kSkSlotArea floats of part slots (one per workgroup, for the partial
+// sums of the tile it starts in the middle of).  Up to kSkMaxGroups
+// workgroups.
+constexpr long kSkMinTokens = 1024;
+constexpr int kSkMaxGroups = 512;
+constexpr int kSkCounterWords = 1024;
+constexpr long kSkSlotArea = 8L << 20;
+inline long sk_region_words(long max_num_tokens) {
+    return max_num_tokens >= kSkMinTokens ? kSkCounterWords + kSkSlotArea : 0;
+}
+inline long meta_region_words(long max_num_tokens, long nslots) {
+    return fused_region_words(max_num_tokens, nslots) + sk_region_words(max_num_tokens);
 }
 // Batches a fused call can take (by size alone): fewer than 24 tokens per
 // segment on average and at most kFusedMaxTokens tokens.  Only their

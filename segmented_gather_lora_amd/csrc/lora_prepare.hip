@@ -47,7 +47,7 @@ constexpr int kSyncGroups = 2 + kFusedMaxParts / 4;
 // Workgroups 1.. of the launch: the fused call's counters and accumulation
 // area start every batch at zero (each fused call also leaves them zero),
 // cleared next to the sort instead of by the sorting workgroup.
-__device__ __forceinline__ void clear_fused_area(const PrepareArgs &a) {
+__device__ __forceinline__ void clear_fused_area(const PrepareArgs &a, int32_t *sk_counters, int sk_words) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     const int stride = (gridDim.x - 1) * kThreads;
     const int first = (blockIdx.x - 1) * kThreads + threadIdx.x;
@@ -57,12 +57,13 @@ __device__ __forceinline__ void clear_fused_area(const PrepareArgs &a) {
         *reinterpret_cast<u32x4 *>(a.sync + kFusedTileWords * tile + word) = z;
     }
     for (int k = first; k < a.acc_floats / 4; k += stride) reinterpret_cast<u32x4 *>(a.acc)[k] = z;
+    for (int k = first; k < sk_words / 4; k += stride) reinterpret_cast<u32x4 *>(sk_counters)[k] = z;
 }
 
-__global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
+__global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a, int32_t *sk_counters, int sk_words) {
     prefetch_kernargs<PrepareArgs>();
     if (blockIdx.x > 0) {
-        clear_fused_area(a);
+        clear_fused_area(a, sk_counters, sk_words);
         return;
     }
     // per wave and key: the running count of the wave's slice (later its
@@ -245,11 +246,12 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a) {
 
 // One sorting workgroup, plus workgroups that clear the fused call's area
 // (about 4 16-byte stores per thread) when the batch can use it.
-hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s) {
-    const long groups = (long)a.sync_tiles * kSyncGroups + a.acc_floats / 4;
+hipError_t launch_prepare(const PrepareArgs &a, int32_t *sk_counters, int sk_words, hipStream_t s) {
+    if (!sk_counters) sk_words = 0;
+    const long groups = (long)a.sync_tiles * kSyncGroups + a.acc_floats / 4 + sk_words / 4;
     long clear = (groups + 4L * kThreads - 1) / (4L * kThreads);
     if (clear > 64) clear = 64;
-    hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(1 + clear)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(1 + clear)), dim3(kThreads), 0, s, a, sk_counters, sk_words);
     return hipGetLastError();
 }
 

@@ -258,45 +258,44 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // scheduled above the wait (the value is an output of this statement).
 __device__ __forceinline__ void after_wait(u32x4 &v) { asm volatile("" : "+v"(v)); }
 
+// The LDS-staged pipeline of one piece of work, shared by the unit-walking
+// and the stream-K kernels: the tile `tr`, the weight rows of row block `rb`,
+// the K range [kbeg, kend).
 template <int NT, int MR, int WR, int STAGES>
-__global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
-    constexpr int WC = 4 / WR;
-    constexpr int BT = 16 * NT, BR = 16 * MR, ROWS = BT + BR;
-    constexpr int INSTR = ROWS / 32;     // load instructions per wave per step
-    constexpr int MT = MR / WR, NTW = NT / WC;
+struct Staged {
+    static constexpr int WC = 4 / WR;
+    static constexpr int BT = 16 * NT, BR = 16 * MR, ROWS = BT + BR;
+    static constexpr int INSTR = ROWS / 32;     // load instructions per wave per step
+    static constexpr int MT = MR / WR, NTW = NT / WC;
+    static constexpr int SLOT = BT * BR;        // floats of one tile's partial sums
+    static constexpr bool SPLIT_H = MT * NTW >= 40;
     static_assert(ROWS % 32 == 0 && MR % WR == 0 && NT % WC == 0, "tile shape");
-    extern __shared__ int smem[];
-    __shared__ int s_wsum[kThreads / kWave];
-    __shared__ __attribute__((aligned(1024))) unsigned char stage[STAGES][ROWS * 128];
+    static_assert((STAGES - 1) * INSTR < 64, "vmcnt range");
+    typedef unsigned char Stage[ROWS * 128];
+    struct Acc {
+        floatx4 v[MT][NTW];
+    };
 
-    const int nslots = a.meta.nslots;
-    const int total = build_tile_table<kThreads>(a.meta, BT, smem, s_wsum);
-
-    const int lane = lane_id(), wave = wave_id();
-    const int wr = wave % WR, wc = wave / WR;
-    const int n16 = lane & 15, g = lane >> 4;
-    const bool atomic = a.k_splits > 1;
-
-    const UnitWalker walk(total * a.row_blocks * a.k_splits);
-    for (int jj = walk.first;; jj += walk.stride) {
-        const int u = walk.unit(jj);
-        if (u < 0) break;
-        const int ks = u % a.k_splits;
-        const int rest = u / a.k_splits;
-        const int rb = rest % a.row_blocks;
-        const TileRef tr = lookup_tile(smem, nslots, rest / a.row_blocks);
-        const int kbeg = ks * a.k_chunk;
-        const int kend = min(kbeg + a.k_chunk, a.hidden);
+    // (The sums are returned by value: the loop then works on values of its
+    // own, which keeps the accumulators in place across iterations.)
+    __device__ __forceinline__ static Acc run(const ShrinkArgs &a, const TileRef &tr, int rb, int kbeg, int kend,
+                                              Stage *stage) {
+        Acc out;
+        floatx4 (&acc)[MT][NTW] = out.v;
+        const int lane = lane_id(), wave = wave_id();
+        const int wr = wave % WR, wc = wave / WR;
+        const int n16 = lane & 15, g = lane >> 4;
         const int nsteps = (kend - kbeg + 63) / 64;
 
         // this lane's source rows: instruction j covers tile rows (wave*INSTR + j)*8 .. +8
+        // every instruction's 8 rows start at a multiple of 8, so the lane's
+        // row index mod 8 and with it its global chunk (landing in slot
+        // lane & 7) are the same for all of them
+        const int chunk_k = 8 * ((lane & 7) ^ ((lane >> 3) & 7));
         const uint16_t *src[INSTR];
-        int chunk_k[INSTR];
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
             const int r = (wave * INSTR + j) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (r & 7);       // global chunk landing in slot lane&7
-            chunk_k[j] = 8 * c;
             if (r < BT) {
                 int p = tr.tile * BT + r;
                 p = p < tr.seg_count ? p : tr.seg_count - 1;
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
             const int sc = step < nsteps ? step : nsteps - 1;   // past the end: reload, never skip
 #pragma unroll
             for (int j = 0; j < INSTR; ++j) {
-                const int k = kbeg + sc * 64 + chunk_k[j];
+                const int k = kbeg + sc * 64 + chunk_k;
                 const uint16_t *gp = src[j] + (k + 8 <= kend ? k : 0);
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gp),
                                                  reinterpret_cast<void *>(&stage[buf][(wave * INSTR + j) * 1024]),
@@ -322,7 +321,6 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
             }
         };
 
-        floatx4 acc[MT][NTW];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -339,49 +337,70 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
             asm volatile("" ::: "memory");
             const unsigned char *sb = stage[s % STAGES];
             const bool mask = s == nsteps - 1 && ((kend - kbeg) & 63) != 0;
-            u32x4 xa[2][NTW], wa[2][MT];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            // the operands of both 32-wide halves of the step, read before the
+            // first MFMA; with SPLIT_H (tiles whose accumulators leave no room
+            // for both) each half is read just before its MFMAs
+            u32x4 xa[SPLIT_H ? 1 : 2][NTW], wa[SPLIT_H ? 1 : 2][MT];
+            auto read_half = [&](int h, int q) {
                 const int c = 2 * g + h;
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const int r = (wc * NTW + nt) * 16 + n16;
-                    xa[h][nt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
+                    xa[q][nt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const int r = BT + (wr * MT + mt) * 16 + n16;
-                    wa[h][mt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
+                    wa[q][mt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
                 }
+            };
+            auto wait_half = [&](int q) {
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) after_wait(xa[q][nt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) after_wait(wa[q][mt]);
+            };
+            if (!SPLIT_H) {
+                read_half(0, 0);
+                read_half(1, SPLIT_H ? 0 : 1);
+                lds_wait();
+                wait_half(0);
+                wait_half(SPLIT_H ? 0 : 1);
             }
-            lds_wait();
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) after_wait(xa[h][nt]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) after_wait(wa[h][mt]);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
+                const int q = SPLIT_H ? 0 : h;
+                if (SPLIT_H) {
+                    read_half(h, 0);
+                    lds_wait();
+                    wait_half(0);
+                }
                 if (mask && kbeg + s * 64 + 8 * (2 * g + h) + 8 > kend) {
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) xa[h][nt] = u32x4{0u, 0u, 0u, 0u};
+                    for (int nt = 0; nt < NTW; ++nt) xa[q][nt] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) wa[h][mt] = u32x4{0u, 0u, 0u, 0u};
+                    for (int mt = 0; mt < MT; ++mt) wa[q][mt] = u32x4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt)
-                        acc[mt][nt] = mfma16x16x32(as_bf16x8(wa[h][mt]), as_bf16x8(xa[h][nt]), acc[mt][nt]);
+                        acc[mt][nt] = mfma16x16x32(as_bf16x8(wa[q][mt]), as_bf16x8(xa[q][nt]), acc[mt][nt]);
             }
             __builtin_amdgcn_s_barrier();   // every wave has read the stage: it may be refilled
         }
         // drain the dummy loads issued past the end before the stages are reused
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();
+        return out;
+    }
 
+    // Writes the piece's sums into buf, scaled.
+    __device__ __forceinline__ static void store(const ShrinkArgs &a, const TileRef &tr, int rb,
+                                                 const floatx4 (&acc)[MT][NTW], bool atomic) {
+        const int lane = lane_id(), wave = wave_id();
+        const int wr = wave % WR, wc = wave / WR;
+        const int n16 = lane & 15, g = lane >> 4;
         // D layout: lane holds rows 4g..4g+3 of m-tile mt for token column n16 of n-tile nt
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -410,6 +429,152 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
                 }
             }
         }
+    }
+};
+
+template <int NT, int MR, int WR, int STAGES>
+__global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
+    using S = Staged<NT, MR, WR, STAGES>;
+    extern __shared__ int smem[];
+    __shared__ int s_wsum[kThreads / kWave];
+    __shared__ __attribute__((aligned(1024))) typename S::Stage stage[STAGES];
+
+    const int nslots = a.meta.nslots;
+    const int total = build_tile_table<kThreads>(a.meta, S::BT, smem, s_wsum);
+    const bool atomic = a.k_splits > 1;
+
+    const UnitWalker walk(total * a.row_blocks * a.k_splits);
+    for (int jj = walk.first;; jj += walk.stride) {
+        const int u = walk.unit(jj);
+        if (u < 0) break;
+        const int ks = u % a.k_splits;
+        const int rest = u / a.k_splits;
+        const int rb = rest % a.row_blocks;
+        const TileRef tr = lookup_tile(smem, nslots, rest / a.row_blocks);
+        const int kbeg = ks * a.k_chunk;
+        const int kend = min(kbeg + a.k_chunk, a.hidden);
+        const typename S::Acc acc = S::run(a, tr, rb, kbeg, kend, stage);
+        S::store(a, tr, rb, acc.v, atomic);
+    }
+}
+
+// Stream-K form of the LDS-staged shrink.  The work is the list of (tile,
+// 64-wide K step) pairs, tile-major.  Workgroups form groups of RB, one per
+// row block of the layer's weight rows; the groups (G of them, about two
+// workgroups per CU in all) take equal contiguous shares of the list, the
+// shares in XCD order (workgroup b sits on XCD b % 8, so consecutive shares
+// and the members of a group stay on one XCD).  The members of a group walk
+// the same tiles and K steps at the same time, so each token row they share
+// comes from HBM once and from that XCD's L2 for the others.  A share cuts
+// at most its first and its last tile:
+//  - the first tile of a share that starts inside the tile is a later part:
+//    each member stores its sums in its own slot (device-scope stores, which
+//    are performed at the device's point of coherence), and once they are
+//    complete (s_waitcnt vmcnt(0), then a barrier) increments the counter of
+//    the tile and row block;
+//  - the part holding the tile's first K step is the last piece of its
+//    share: it waits until the counter shows every later part, adds their
+//    slots (device-scope loads) to its own sums and stores the tile, then
+//    sets the counter back to zero for the next launch.
+// A later part is always the first piece of its share and never waits, so
+// the waits end whenever every workgroup runs; each share has the same
+// number of K steps, so every CU finishes at about the same time whatever
+// the number of tiles.  A wait that passes kSkSpinLimit polls sets
+// LORA_ERR_SYNC and goes on (the result is then unspecified).
+constexpr int kSkSpinLimit = 1 << 18;
+// Cache policy of the slot accesses: device scope (sc1), the bits an
+// agent-scope atomic load or store carries.
+constexpr int kCpolDevice = 16;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+template <int NT, int MR, int WR, int STAGES>
+__global__ __launch_bounds__(kThreads) void shrink_sk_kernel(ShrinkArgs a, SkArgs sk) {
+    using S = Staged<NT, MR, WR, STAGES>;
+    extern __shared__ int smem[];
+    __shared__ int s_wsum[kThreads / kWave];
+    __shared__ __attribute__((aligned(1024))) typename S::Stage stage[STAGES];
+
+    const int nslots = a.meta.nslots;
+    const int total = build_tile_table<kThreads>(a.meta, S::BT, smem, s_wsum);
+    const int tid = threadIdx.x;
+    const int RB = a.row_blocks;
+    const int nsteps = (a.hidden + 63) / 64;
+    const long W = (long)total * nsteps;
+    // groups per XCD (the launcher makes it at least one); with fewer steps
+    // than groups only the first W groups are used, so that every share in
+    // use holds at least one step
+    const int gx = (int)(gridDim.x / kNumXcd) / RB;
+    const int i = (int)(blockIdx.x / kNumXcd);
+    if (i >= gx * RB) return;
+    const int gq = (int)(blockIdx.x % kNumXcd) * gx + i / RB, r = i % RB;
+    const int G = W < (long)(kNumXcd * gx) ? (int)W : kNumXcd * gx;
+    if (gq >= G) return;
+    const long end = W * (gq + 1) / G;
+    // the group whose share holds step `it` of the list
+    auto owner = [&](long it) { return (int)(((it + 1) * G - 1) / W); };
+    // member r of group k: its slot
+    auto slot_rsrc = [&](int k) {
+        return __builtin_amdgcn_make_buffer_rsrc(sk.slots + (long)(k * RB + r) * S::SLOT, 0, S::SLOT * 4, 0x00020000);
+    };
+
+    for (long cur = W * gq / G; cur < end;) {
+        const int t = (int)(cur / nsteps);
+        const int s0 = (int)(cur - (long)t * nsteps);
+        const int s1 = (int)min((long)nsteps, (long)s0 + (end - cur));
+        cur += s1 - s0;
+        const TileRef tr = lookup_tile(smem, nslots, t);
+        typename S::Acc res = S::run(a, tr, r, 64 * s0, min(64 * s1, a.hidden), stage);
+        floatx4 (&acc)[S::MT][S::NTW] = res.v;
+        if (s0 > 0 || s1 < nsteps) {
+            const long first = (long)t * nsteps;
+            const int ga = owner(first);
+            int32_t *count = sk.counters + (ga + 1) * RB + r;   // the first share boundary inside the tile
+            if (s0 > 0) {
+                const __amdgpu_buffer_rsrc_t slot = slot_rsrc(gq);
+#pragma unroll
+                for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < S::NTW; ++nt)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[mt][nt]), slot, 16 * tid,
+                                                               (mt * S::NTW + nt) * 16 * kThreads, kCpolDevice);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                __syncthreads();
+                if (tid == 0) __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
+            const int gb = owner(first + nsteps - 1);
+            if (tid == 0) {
+                int n = 0;
+                while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gb - gq &&
+                       n < kSkSpinLimit) {
+                    ++n;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                if (n == kSkSpinLimit)
+                    __hip_atomic_store(sk.status, (int)LORA_ERR_SYNC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            // the later parts' sums, up to 16 16-byte loads in flight at a time
+            constexpr int P = S::MT * S::NTW;
+            constexpr int B = P < 16 ? P : 16;
+            for (int k = gq + 1; k <= gb; ++k) {
+                const __amdgpu_buffer_rsrc_t slot = slot_rsrc(k);
+#pragma unroll
+                for (int p0 = 0; p0 < P; p0 += B) {
+                    floatx4 v[B];
+#pragma unroll
+                    for (int q = 0; q < B; ++q)
+                        if (p0 + q < P)
+                            v[q] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                   slot, 16 * tid, (p0 + q) * 16 * kThreads, kCpolDevice));
+#pragma unroll
+                    for (int q = 0; q < B; ++q)
+                        if (p0 + q < P) acc[(p0 + q) / S::NTW][(p0 + q) % S::NTW] += v[q];
+                }
+            }
+        }
+        S::store(a, tr, r, acc, false);
     }
 }
 
@@ -473,29 +638,37 @@ ShrinkFn pick(int nt, int wk, int mt) {
 
 
 // LDS-staged configurations: tokens x rows per workgroup, wave layout, stages.
+typedef void (*SkFn)(ShrinkArgs, SkArgs);
 struct StagedCfg {
     int nt, mr, wr, stages;
     bool automatic;   // eligible for the automatic choice
     ShrinkFn fn;
+    SkFn sk;          // the same tile in the stream-K kernel
 };
 const StagedCfg kStaged[] = {
-    {4, 12, 4, 3, true, shrink_lds_kernel<4, 12, 4, 3>},    // 0: 64 tokens x 192 rows
-    {8, 12, 4, 3, false, shrink_lds_kernel<8, 12, 4, 3>},   // 1: 128 x 192 (one wave per SIMD: slow)
-    {4, 8, 4, 4, true, shrink_lds_kernel<4, 8, 4, 4>},      // 2: 64 x 128
-    {4, 4, 4, 4, true, shrink_lds_kernel<4, 4, 4, 4>},      // 3: 64 x 64
-    {4, 2, 2, 4, true, shrink_lds_kernel<4, 2, 2, 4>},      // 4: 64 x 32
-    {2, 12, 4, 4, true, shrink_lds_kernel<2, 12, 4, 4>},    // 5: 32 x 192
-    {8, 4, 4, 4, true, shrink_lds_kernel<8, 4, 4, 4>},      // 6: 128 x 64
-    {8, 2, 2, 4, true, shrink_lds_kernel<8, 2, 2, 4>},      // 7: 128 x 32
-    {2, 4, 4, 4, true, shrink_lds_kernel<2, 4, 4, 4>},      // 8: 32 x 64
-    {2, 2, 2, 4, true, shrink_lds_kernel<2, 2, 2, 4>},      // 9: 32 x 32
-    {4, 6, 2, 5, true, shrink_lds_kernel<4, 6, 2, 5>},      // 10: 64 x 96
-    {8, 6, 2, 4, true, shrink_lds_kernel<8, 6, 2, 4>},      // 11: 128 x 96
-    {8, 8, 4, 4, false, shrink_lds_kernel<8, 8, 4, 4>},     // 12: 128 x 128, 4 stages (one per CU)
-    {8, 8, 4, 2, true, shrink_lds_kernel<8, 8, 4, 2>},      // 13: 128 x 128, 2 stages (two per CU)
-    {4, 6, 2, 3, false, shrink_lds_kernel<4, 6, 2, 3>},     // 14: 64 x 96, 3 stages (two per CU)
+    {4, 12, 4, 3, true, shrink_lds_kernel<4, 12, 4, 3>, shrink_sk_kernel<4, 12, 4, 3>},    // 0: 64 tokens x 192 rows
+    {8, 12, 4, 3, false, shrink_lds_kernel<8, 12, 4, 3>, shrink_sk_kernel<8, 12, 4, 3>},   // 1: 128 x 192 (one wave per SIMD: slow)
+    {4, 8, 4, 4, true, shrink_lds_kernel<4, 8, 4, 4>, shrink_sk_kernel<4, 8, 4, 4>},      // 2: 64 x 128
+    {4, 4, 4, 4, true, shrink_lds_kernel<4, 4, 4, 4>, shrink_sk_kernel<4, 4, 4, 4>},      // 3: 64 x 64
+    {4, 2, 2, 4, true, shrink_lds_kernel<4, 2, 2, 4>, shrink_sk_kernel<4, 2, 2, 4>},      // 4: 64 x 32
+    {2, 12, 4, 4, true, shrink_lds_kernel<2, 12, 4, 4>, shrink_sk_kernel<2, 12, 4, 4>},    // 5: 32 x 192
+    {8, 4, 4, 4, true, shrink_lds_kernel<8, 4, 4, 4>, shrink_sk_kernel<8, 4, 4, 4>},      // 6: 128 x 64
+    {8, 2, 2, 4, true, shrink_lds_kernel<8, 2, 2, 4>, shrink_sk_kernel<8, 2, 2, 4>},      // 7: 128 x 32
+    {2, 4, 4, 4, true, shrink_lds_kernel<2, 4, 4, 4>, shrink_sk_kernel<2, 4, 4, 4>},      // 8: 32 x 64
+    {2, 2, 2, 4, true, shrink_lds_kernel<2, 2, 2, 4>, shrink_sk_kernel<2, 2, 2, 4>},      // 9: 32 x 32
+    {4, 6, 2, 5, true, shrink_lds_kernel<4, 6, 2, 5>, shrink_sk_kernel<4, 6, 2, 5>},      // 10: 64 x 96
+    {8, 6, 2, 4, true, shrink_lds_kernel<8, 6, 2, 4>, shrink_sk_kernel<8, 6, 2, 4>},      // 11: 128 x 96
+    {8, 8, 4, 4, false, shrink_lds_kernel<8, 8, 4, 4>, shrink_sk_kernel<8, 8, 4, 4>},     // 12: 128 x 128, 4 stages (one per CU)
+    {8, 8, 4, 2, true, shrink_lds_kernel<8, 8, 4, 2>, shrink_sk_kernel<8, 8, 4, 2>},      // 13: 128 x 128, 2 stages (two per CU)
+    {4, 6, 2, 3, false, shrink_lds_kernel<4, 6, 2, 3>, shrink_sk_kernel<4, 6, 2, 3>},     // 14: 64 x 96, 3 stages (two per CU)
+    {4, 6, 2, 7, false, shrink_lds_kernel<4, 6, 2, 7>, shrink_sk_kernel<4, 6, 2, 7>},     // 15: 64 x 96, 7 stages
+    {2, 4, 4, 10, false, shrink_lds_kernel<2, 4, 4, 10>, shrink_sk_kernel<2, 4, 4, 10>},   // 16: 32 x 64, 10 stages
+    {4, 4, 4, 8, false, shrink_lds_kernel<4, 4, 4, 8>, shrink_sk_kernel<4, 4, 4, 8>},     // 17: 64 x 64, 8 stages
+    {2, 2, 2, 12, false, shrink_lds_kernel<2, 2, 2, 12>, shrink_sk_kernel<2, 2, 2, 12>},   // 18: 32 x 32, 12 stages
 };
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
+
+constexpr int kSkMinSteps = 8;   // K steps per workgroup share, at least
 
 }  // namespace
 
@@ -509,7 +682,10 @@ namespace {
 
 struct ShrinkPlan {
     bool staged;
+    bool sk;          // stream-K (sk_fn)
     ShrinkFn fn;
+    SkFn sk_fn;
+    long slot_floats; // stream-K: floats of one part slot
     int tile_tokens, row_blocks, k_splits, k_chunk;
     long units_upper;
 };
@@ -522,11 +698,13 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     const int max_ks = (hidden + 255) / 256;
 
     pl.staged = cfg.variant == 3 || (cfg.variant == 0 && avg >= 24);
+    pl.sk = false;
     int rows_per_wg;
+    int idx = -1;
     int forced_ks = cfg.k_splits;
     int model_ks = 1;
     if (pl.staged) {
-        int idx = cfg.staged_cfg;
+        idx = cfg.staged_cfg;
         if (idx <= 0 || idx > kNumStaged) {
             // Cost model: a unit streams (tokens + rows) x K_chunk bf16 through
             // LDS at about the same rate on every CU, so the time goes as
@@ -590,6 +768,28 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     pl.k_splits = ks;
     pl.k_chunk = chunk;
     pl.units_upper = (long)tiles_upper * pl.row_blocks * ks;
+
+    // Stream-K, with the same tile, for batches of at least kSkMinTokens
+    // tokens (whose library-owned area holds the part slots): where the
+    // model splits K because the units alone would not fill the GPU (the
+    // partial sums are then combined through the slots instead of float
+    // atomics into a cleared buffer), and for tiles of at most 32 tokens,
+    // whose many short, uneven segments leave some CUs with one unit more
+    // than others.  LORA_SHRINK_SK=2 forces it for any staged batch that
+    // size, LORA_SHRINK_SK=1 turns it off.
+    const bool sk_auto = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0 &&
+                         (ks > 1 || pl.tile_tokens <= 32);
+    if (pl.staged && n >= kSkMinTokens && (cfg.stream_k == 2 || sk_auto)) {
+        const StagedCfg &c = kStaged[idx];
+        pl.sk = true;
+        pl.fn = nullptr;
+        pl.sk_fn = c.sk;
+        pl.slot_floats = 256 * c.nt * c.mr;
+        pl.k_splits = 1;
+        pl.k_chunk = (hidden + 63) / 64 * 64;
+        // K steps of the list, at most
+        pl.units_upper = (long)tiles_upper * ((hidden + 63) / 64);
+    }
     return pl;
 }
 
@@ -597,14 +797,51 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
 
 int shrink_launches(int n, int nslots, int rows, int hidden, bool overwrite, const ShrinkTuning &cfg) {
     if (n < 1) return 0;
-    return (overwrite && plan_shrink(n, nslots, rows, hidden, cfg).k_splits > 1) ? 2 : 1;
+    const ShrinkPlan pl = plan_shrink(n, nslots, rows, hidden, cfg);
+    return (overwrite && !pl.sk && pl.k_splits > 1) ? 2 : 1;
 }
 
-hipError_t launch_shrink(const ShrinkArgs &in, const ShrinkTuning &cfg, hipStream_t s) {
+hipError_t launch_shrink(const ShrinkArgs &in, const SkArgs &sk, const ShrinkTuning &cfg, hipStream_t s) {
     ShrinkArgs a = in;
     const int n = a.num_tokens;
     const int nslots = a.meta.nslots;
-    const ShrinkPlan pl = plan_shrink(n, nslots, a.rows, a.hidden, cfg);
+    ShrinkPlan pl = plan_shrink(n, nslots, a.rows, a.hidden, cfg);
+    if (pl.sk && (!sk.slots || !sk.counters || !sk.status)) {
+        // the area has no stream-K part (cannot happen for a batch of this
+        // size, which the region was bound for): the unit-walking kernel
+        ShrinkTuning c = cfg;
+        c.stream_k = 1;
+        pl = plan_shrink(n, nslots, a.rows, a.hidden, c);
+    }
+    if (pl.sk) {
+        a.row_blocks = pl.row_blocks;
+        a.k_splits = 1;
+        a.k_chunk = pl.k_chunk;
+        a.num_units = 0;
+        a.meta.lds_tokens = 0;
+        const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1);
+        const int rb = pl.row_blocks;
+        long grid = resident_grid(reinterpret_cast<const void *>(pl.sk_fn), kThreads, lds);
+        if (grid > kSkMaxGroups) grid = kSkMaxGroups;
+        if (grid > kSkSlotArea / pl.slot_floats) grid = kSkSlotArea / pl.slot_floats;
+        if (cfg.grid_cap > 0) {
+            if (grid > cfg.grid_cap) grid = cfg.grid_cap;   // tuning and tests: exactly this many
+        } else {
+            const long by_work = pl.units_upper * rb / kSkMinSteps;
+            if (grid > by_work) grid = by_work;
+        }
+        // whole groups of rb workgroups on every XCD, and a counter per
+        // share boundary and row block
+        long gx = grid / kNumXcd / rb;
+        if ((kNumXcd * gx + 1) * rb > kSkCounterWords) gx = (kSkCounterWords / rb - 1) / kNumXcd;
+        if (gx >= 1) {
+            hipLaunchKernelGGL(pl.sk_fn, dim3((unsigned)(kNumXcd * gx * rb)), dim3(kThreads), lds, s, a, sk);
+            return hipGetLastError();
+        }
+        ShrinkTuning c = cfg;   // too many row blocks for the resident workgroups: walk units
+        c.stream_k = 1;
+        pl = plan_shrink(n, nslots, a.rows, a.hidden, c);
+    }
     a.row_blocks = pl.row_blocks;
     a.k_splits = pl.k_splits;
     a.k_chunk = pl.k_chunk;

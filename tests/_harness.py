@@ -250,6 +250,7 @@ def run_and_check(wl: workloads.Workload, add_inputs: bool = True, sample: int |
         torch.cuda.synchronize()
         if fused:
             check_sync_clear(meta, n)
+        check_sk_clear(meta)
         buf_g = buf.cpu().numpy()
         y_g = bits(y)
         y0b = bits(y0full)
@@ -297,6 +298,21 @@ def check_sync_clear(meta, n: int) -> None:
     acc_off = off + 4 * sync_words(meta.max_num_tokens, meta.max_loras)
     acc = meta.region[acc_off:acc_off + 4 * 64 * min(n, 24576)].view(torch.int32).cpu().numpy()
     assert np.all(acc == 0), "accumulation area not cleared: %d nonzero words" % int((acc != 0).sum())
+    assert int(v["status"][0]) in (0, lib().LORA_ERR_ID_RANGE), "status %d" % int(v["status"][0])
+
+
+def check_sk_clear(meta) -> None:
+    """The stream-K shrink's counters (1024 words after the LoRA-major part
+    slots of a region bound for at least 1024 tokens) are zero after every
+    launch, and no wait timed out."""
+    N, ml = meta.max_num_tokens, meta.max_loras
+    if N < 1024:
+        return
+    v = meta.views()
+    off = meta.struct.sync - meta.region.data_ptr()
+    words = sync_words(N, ml) + 64 * min(N, 24576) + 16 * 64 * min(N, 2048)
+    c = meta.region[off + 4 * words:off + 4 * (words + 1024)].view(torch.int32).cpu().numpy()
+    assert np.all(c == 0), "stream-K counters not reset: %d nonzero" % int((c != 0).sum())
     assert int(v["status"][0]) in (0, lib().LORA_ERR_ID_RANGE), "status %d" % int(v["status"][0])
 
 

@@ -25,7 +25,7 @@ def _wl(n, max_loras, layers, hidden=4096):
     return types.SimpleNamespace(mapping=mapping, spec=spec, layers=ls)
 
 
-def test_launch_count_query():
+def test_launch_count_query(monkeypatch):
     """The library's own answer (host only) at the edges of the one-launch range."""
     import segmented_gather_lora_amd as sgl
     q = sgl.lora_shrink_expand_launches
@@ -39,8 +39,12 @@ def test_launch_count_query():
     assert q(256, 32, 4096, 3, 32, False) in sep
     assert q(23 * 1024, 1023, 4096, 1, 8, False) == 1 and q(23 * 1024 + 1, 1023, 4096, 1, 8, False) in sep
     assert q(16384, 128, 8192, 3, 128, False) == 2 and q(16384, 128, 8192, 3, 128, True) == 3
-    # a split-K shrink into a fresh buffer zeroes the active rows first (Zipf's down layer)
+    # the stream-K shrink (batches of 1024 tokens or more) adds its parts up without atomics
+    assert q(4096, 64, 14336, 1, 32, False) == 2 and q(4096, 64, 14336, 1, 32, True) == 3
+    # without it, a split-K shrink into a fresh buffer zeroes the active rows first (Zipf's down layer)
+    monkeypatch.setenv("LORA_SHRINK_SK", "1")
     assert q(4096, 64, 14336, 1, 32, False) == 3 and q(4096, 64, 14336, 1, 32, True) == 4
+    monkeypatch.delenv("LORA_SHRINK_SK")
     for bad in [(0, 32, 4096, 3, 16), (256, 0, 4096, 3, 16), (256, 32, 4096, 0, 16), (256, 32, 4096, 3, 12),
                 (256, 32, 12, 3, 16)]:
         with pytest.raises(sgl.LoraError):

@@ -395,6 +395,35 @@ def test_shrink_staged_full_rows(monkeypatch):
     H.run_and_check(wl, add_inputs=True)
 
 
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5, 9, 10, 11, 14, 15])
+@pytest.mark.parametrize("slices,rank,hidden", [((32,), 32, 1000), ((72, 40, 104), 32, 1000),
+                                                ((64, 64, 64), 64, 520), ((256, 128, 128), 128, 712)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_shrink_stream_k(cfg, slices, rank, hidden, fused, monkeypatch):
+    """The stream-K shrink with every kind of staged tile, on 32 to 384
+    weight rows (one or several row blocks), K not a multiple of 64, shares
+    that cut tiles into two or more parts, -1 ids; accumulating into buf
+    (lora_shrink) and writing a fresh one (lora_shrink_expand)."""
+    monkeypatch.setenv("LORA_SHRINK_SK", "2")
+    monkeypatch.setenv("LORA_SHRINK_STAGED", str(cfg))
+    wl = workloads.random_case(300 + rank + len(slices), 1500, hidden, slices, rank, 6, bias=True,
+                               neg_fraction=0.1)
+    print("stream-K shrink", cfg, slices, rank, hidden, fused, flush=True)
+    H.run_and_check(wl, add_inputs=True, fused=fused)
+
+
+@pytest.mark.parametrize("grid", [8, 64, 256])
+def test_shrink_stream_k_many_parts(grid, monkeypatch):
+    """Stream-K with more workgroups than the work needs: shares of a step or
+    less, tiles cut into many parts, workgroups with nothing to do."""
+    monkeypatch.setenv("LORA_SHRINK_SK", "2")
+    monkeypatch.setenv("LORA_SHRINK_GRID", str(grid))
+    wl = workloads.random_case(340 + grid, 1100, 712, (64, 64), 32, 3, neg_fraction=0.05)
+    print("stream-K shrink grid", grid, flush=True)
+    H.run_and_check(wl, add_inputs=True)
+    H.run_and_check(wl, add_inputs=False, fused=True)
+
+
 # ------------------------------------------------------------------ logits and embedding paths
 
 @pytest.mark.parametrize("add_inputs", [True, False])
