@@ -87,24 +87,25 @@ def kernel_source_hash() -> str:
 # ------------------------------------------------------------------ dispatch plan
 
 class Plan:
-    """The library calls a run makes, in order, with the kernel launches each
-    makes (from the library's own launch-count query): rocprofv3's kernel
-    trace is matched against it to give per-workload, per-layer durations."""
+    """The library calls a run makes, in order, with the kinds of the kernels
+    each launches (from the library's own launch-count queries): rocprofv3's
+    kernel trace is matched against it to give per-workload, per-layer
+    durations."""
 
     def __init__(self):
-        self.calls = []          # [workload, phase, tag, launches]
+        self.calls = []          # [workload, phase, tag, kernel kinds, times]
         self.phase = "setup"
         self.workload = ""
 
-    def add(self, tag: str, launches: int, times: int = 1):
-        if self.calls and self.calls[-1][:3] == [self.workload, self.phase, tag] and \
-                self.calls[-1][3] == launches:
+    def add(self, tag: str, kinds, times: int = 1):
+        kinds = list(kinds)
+        if self.calls and self.calls[-1][:4] == [self.workload, self.phase, tag, kinds]:
             self.calls[-1][4] += times
         else:
-            self.calls.append([self.workload, self.phase, tag, launches, times])
+            self.calls.append([self.workload, self.phase, tag, kinds, times])
 
     def replay(self, seq, times: int):
-        """A captured sequence of (tag, launches) replayed `times` times."""
+        """A captured sequence of (tag, kinds) replayed `times` times."""
         for _ in range(times):
             for tag, k in seq:
                 self.add(tag, k)
@@ -149,19 +150,19 @@ class DeviceSet:
     def prepare(self):
         import segmented_gather_lora_amd as sgl
         sgl.lora_prepare_meta(self.mapping, self.meta)
-        PLAN.add("prepare", 1)
+        PLAN.add("prepare", prepare_kinds(self.n, self.wl.spec.max_loras))
 
     def shrink(self, li):
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_shrink(d["x"], d["a"], d["buf"], self.meta, d["scale"])
-        PLAN.add("shrink%d" % li, 1)
+        PLAN.add("shrink%d" % li, ["shrink"])
 
     def expand(self, li):
         import segmented_gather_lora_amd as sgl
         d = self.layers[li]
         sgl.lora_expand(d["buf"], d["b"], d["bias"], d["y"], self.meta, offset_start=0, add_inputs=True)
-        PLAN.add("expand%d" % li, 1)
+        PLAN.add("expand%d" % li, ["expand"])
 
     def linear(self, li):
         """add_lora_linear of one layer: one lora_shrink_expand call."""
@@ -169,7 +170,7 @@ class DeviceSet:
         d = self.layers[li]
         sgl.lora_shrink_expand(d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta, d["scale"],
                                offset_start=0, add_inputs=True)
-        PLAN.add("linear%d" % li, launches(self.wl, li, False))
+        PLAN.add("linear%d" % li, call_kinds(self.wl, li, False))
 
     def prepare_linear(self, li):
         """prepare + add_lora_linear of one layer: one lora_prepare_shrink_expand call."""
@@ -177,7 +178,7 @@ class DeviceSet:
         d = self.layers[li]
         sgl.lora_prepare_shrink_expand(self.mapping, d["x"], d["a"], d["b"], d["bias"], d["buf"], d["y"], self.meta,
                                        d["scale"], offset_start=0, add_inputs=True)
-        PLAN.add("preplinear%d" % li, launches(self.wl, li, True))
+        PLAN.add("preplinear%d" % li, call_kinds(self.wl, li, True))
 
     def step(self, path: str = "prepare_fused"):
         first = 0
@@ -211,6 +212,22 @@ def launches(wl, li: int, with_prepare: bool) -> int:
 
 def one_launch(wl, li: int, with_prepare: bool) -> bool:
     return launches(wl, li, with_prepare) == 1
+
+
+def prepare_kinds(n: int, max_loras: int):
+    """Kernels of lora_prepare_meta for n tokens: one sorting launch, or the
+    rank and place launches of the several-workgroup sort."""
+    import segmented_gather_lora_amd as sgl
+    return ["prepare"] if sgl.lora_prepare_meta_launches(n, max_loras) == 1 else ["prepare_rank", "prepare_place"]
+
+
+def call_kinds(wl, li: int, with_prepare: bool):
+    """Kernels of lora_shrink_expand (lora_prepare_shrink_expand) for layer li,
+    in launch order."""
+    if launches(wl, li, with_prepare) == 1:
+        return ["one_launch"]
+    zero = ["zero"] if launches(wl, li, False) == 3 else []
+    return (prepare_kinds(wl.mapping.numel(), wl.spec.max_loras) if with_prepare else []) + zero + ["shrink", "expand"]
 
 
 def set_bytes(wl) -> int:
@@ -315,9 +332,13 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 def _kind_of(name: str):
     if "prepare_kernel" in name:
         return "prepare"
+    if "prepare_rank_kernel" in name:
+        return "prepare_rank"
+    if "prepare_place_kernel" in name:
+        return "prepare_place"
     if "zero_rows_kernel" in name:
         return "zero"
-    if "shrink_kernel" in name or "shrink_lds_kernel" in name:
+    if "shrink_kernel" in name or "shrink_lds_kernel" in name or "shrink_sk_kernel" in name:
         return "shrink"
     if "expand_kernel" in name:
         return "expand"
@@ -330,21 +351,6 @@ def _kind_of(name: str):
     return None
 
 
-def _expected_kinds(tag: str, k: int):
-    """Kernel kinds a call of `tag` making k launches dispatches, in order."""
-    if tag.startswith(("linear", "preplinear")):
-        if k == 1:
-            return ["one_launch"]
-        kinds = ["prepare"] if tag.startswith("prep") else []
-        if k - len(kinds) == 3:
-            kinds.append("zero")
-        return kinds + ["shrink", "expand"]
-    for p in ("prepare", "shrink", "expand", "probe_read", "probe_empty"):
-        if tag.startswith(p):
-            return [p]
-    raise ValueError(tag)
-
-
 def summarize_trace(trace_csv: str, plan_json: str, out_md: str, command: str) -> dict:
     """Per-workload, per-layer kernel durations from one rocprofv3
     --kernel-trace run of bench.py --dispatch-plan: the library's dispatches,
@@ -355,8 +361,7 @@ def summarize_trace(trace_csv: str, plan_json: str, out_md: str, command: str) -
     rows.sort(key=lambda r: int(r[key]))
     plan = json.load(open(plan_json))["calls"]
     expect = []
-    for wl, phase, tag, k, times in plan:
-        kinds = _expected_kinds(tag, k)
+    for wl, phase, tag, kinds, times in plan:
         for _ in range(times):
             for kind in kinds:
                 expect.append((wl, phase, tag, kind))
@@ -372,7 +377,7 @@ def summarize_trace(trace_csv: str, plan_json: str, out_md: str, command: str) -
         if phase not in ("timed", "per_call"):
             continue
         layer = "".join(ch for ch in tag if ch.isdigit())
-        label = kind if kind in ("prepare", "probe_read", "probe_empty") else "%s%s" % (kind, layer)
+        label = kind if kind.startswith(("prepare", "probe")) else "%s%s" % (kind, layer)
         k2 = (wl, phase, tag, label)
         stats[k2].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         names[k2] = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
@@ -429,12 +434,12 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
     import workloads
     specs = workloads.WORKLOADS[workload].layers
     layers_of = {"shrink": [i for i, L in enumerate(specs) if not L.expand_only],
-                 "expand": list(range(len(specs))), "prepare": [0], "preplinear": [0], "copy": [0]}
+                 "expand": list(range(len(specs))), "prepare": [0], "prepare_rank": [0], "prepare_place": [0],
+                 "preplinear": [0], "copy": [0]}
     layers_of["linear"] = [i for i in layers_of["shrink"] if i > 0] or [0]
     # the zeroing of buf's rows runs only for layers whose call splits the shrink over K
     wl = workloads.make_workload(workload)
-    layers_of["zero"] = [i for i in layers_of["shrink"]
-                         if launches(wl, i, i == 0) == (4 if i == 0 else 3)] or [0]
+    layers_of["zero"] = [i for i in layers_of["shrink"] if launches(wl, i, False) == 3] or [0]
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -453,7 +458,7 @@ def summarize_pmc(workload: str, fetch_csv: str, write_csv: str, out_json: str, 
                 lays = layers_of[kind]
                 li = lays[seen[kind] % len(lays)]
                 seen[kind] += 1
-                key = kind if kind in ("prepare", "copy") else "%s%d" % (kind, li)
+                key = kind if kind.startswith("prepare") or kind == "copy" else "%s%d" % (kind, li)
                 vals[key].append(float(r["Counter_Value"]) * 1024.0)
         return vals
 
@@ -563,7 +568,7 @@ def probe_read(nbytes: int, copies: int) -> dict:
     def run():
         for b in bufs:
             sgl.lora_probe_read(b, PROBE_WG, sink)
-            PLAN.add("probe_read", 1)
+            PLAN.add("probe_read", ["probe_read"])
     run()
     g, seq = capture(run)
     g.replay()
@@ -581,7 +586,7 @@ def probe_empty() -> float:
     def run():
         for _ in range(64):
             sgl.lora_probe_empty(EMPTY_WG)
-            PLAN.add("probe_empty", 1)
+            PLAN.add("probe_empty", ["probe_empty"])
     run()
     g, seq = capture(run)
     g.replay()

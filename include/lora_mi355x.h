@@ -287,13 +287,22 @@ int lora_shrink_expand_noalloc(const void *x, int64_t ldx, int num_tokens, int h
  * average, num_slices * rank <= 64, rank <= 64, and with the prepare at most
  * 2048 tokens), else the separate calls' count: prepare (with_prepare), the
  * zeroing of buf's active rows when the shrink is split over K chunks, shrink
- * and expand.  A batch whose every id is -1 still makes these launches (they
+ * and expand (prepare: lora_prepare_meta_launches).  A batch whose every id
+ * is -1 still makes these launches (they
  * touch nothing).  Host only: no device work, no HIP call.  Negative
  * lora_status for arguments the calls themselves would reject.  A measurement
  * aid: it tells which kernel durations make up a call.
  */
 int lora_shrink_expand_launches(int num_tokens, int max_loras, int hidden, int num_slices, int rank,
                                 int with_prepare);
+
+/* Kernel launches lora_prepare_meta makes for a batch of num_tokens tokens
+ * with the metadata sized for max_loras: 2 when several workgroups sort it
+ * (at least 4096 tokens, and enough of them for the id width that one
+ * workgroup would take longer: one launch ranks the tokens of each chunk, the
+ * next places them), else 1.  Host only.  LORA_ERR_NUM_TOKENS /
+ * LORA_ERR_MAX_LORAS for arguments out of range.  A measurement aid. */
+int lora_prepare_meta_launches(int num_tokens, int max_loras);
 
 /* Static description of a status code. */
 const char *lora_status_string(int status);

@@ -6,8 +6,9 @@ mirror the C ABI in include/lora_mi355x.h:
 
     lora_meta_bytes, lora_meta_bind, lora_prepare_meta, lora_shrink,
     lora_expand, lora_shrink_expand, lora_prepare_shrink_expand,
-    lora_shrink_expand_launches, lora_status_string, and the measurement aids
-    lora_probe_read, lora_probe_empty
+    lora_shrink_expand_noalloc, lora_status_string, and the measurement aids
+    lora_shrink_expand_launches, lora_prepare_meta_launches, lora_probe_read,
+    lora_probe_empty
 
 plus ``LoraMeta``, a holder that owns one device region sized by
 ``lora_meta_bytes`` (LoRAKernelMeta.make on the "lora_kernel_metadata" page)
@@ -44,6 +45,7 @@ LORA_MAX_RANK = 128
 
 EXPORTED = ("lora_meta_bytes", "lora_meta_bind", "lora_prepare_meta", "lora_shrink",
             "lora_expand", "lora_shrink_expand", "lora_prepare_shrink_expand", "lora_shrink_expand_launches",
+            "lora_prepare_meta_launches",
             "lora_status_string", "lora_probe_read", "lora_probe_empty", "lora_shrink_expand_noalloc")
 
 
@@ -99,6 +101,8 @@ def _load() -> ctypes.CDLL:
                                                ctypes.POINTER(lora_meta_t), ctypes.c_float, P]
     lib.lora_shrink_expand_launches.restype = i32
     lib.lora_shrink_expand_launches.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.lora_prepare_meta_launches.restype = i32
+    lib.lora_prepare_meta_launches.argtypes = [i32, i32]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [i32]
     lib.lora_probe_read.restype = i32
@@ -139,6 +143,14 @@ def lora_shrink_expand_launches(num_tokens: int, max_loras: int, hidden: int, nu
                                             int(rank), 1 if with_prepare else 0)
     if st < 0:
         raise LoraError(st, "lora_shrink_expand_launches")
+    return st
+
+
+def lora_prepare_meta_launches(num_tokens: int, max_loras: int) -> int:
+    """Kernel launches of lora_prepare_meta for a batch of this size (host only)."""
+    st = _lib().lora_prepare_meta_launches(int(num_tokens), int(max_loras))
+    if st < 0:
+        raise LoraError(st, "lora_prepare_meta_launches")
     return st
 
 

@@ -394,8 +394,14 @@ int lora_shrink_expand_launches(int num_tokens, int max_loras, int hidden, int n
     if (env_int("LORA_FUSED") >= 0 &&
         one_launch_range(num_tokens, (long)max_loras + 1, num_slices * rank, rank, with_prepare != 0))
         return 1;
-    return (with_prepare ? 1 : 0) +
+    return (with_prepare ? prepare_launches(num_tokens, max_loras) : 0) +
            shrink_launches(num_tokens, max_loras + 1, num_slices * rank, hidden, true, shrink_tuning()) + 1;
+}
+
+int lora_prepare_meta_launches(int num_tokens, int max_loras) {
+    if (num_tokens < 0 || num_tokens > LORA_MAX_TOKENS) return LORA_ERR_NUM_TOKENS;
+    if (max_loras < 1 || max_loras > LORA_MAX_LORAS) return LORA_ERR_MAX_LORAS;
+    return prepare_launches(num_tokens, max_loras);
 }
 
 int lora_prepare_shrink_expand(const int32_t *mapping, int num_tokens, const void *x, int64_t ldx, int hidden,

@@ -397,6 +397,9 @@ inline long persistent_grid(long units, long cap, const void *fn, int threads, s
 // Also zeroes the stream-K shrink's counters (sk_words words at sk_counters;
 // none when sk_words is 0).
 hipError_t launch_prepare(const PrepareArgs &a, int32_t *sk_counters, int sk_words, hipStream_t s);
+// Kernel launches launch_prepare makes for a batch of n tokens (host only):
+// 2 for batches sorted by several workgroups, else 1.
+int prepare_launches(int n, int max_loras);
 hipError_t launch_shrink(const ShrinkArgs &a, const SkArgs &sk, const ShrinkTuning &cfg, hipStream_t s);
 // Kernel launches launch_shrink makes for these sizes (host only): 2 when a
 // fresh buffer (overwrite) is combined from K chunks and its rows are zeroed

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a, int32_
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) {   // one round trip for the chunk (addresses clamped)
             const int t = t0 + (c0 + q) * kWave + lane;
-            ids[q] = a.mapping[t < n ? t : n - 1];
+            if (c0 + q < steps) ids[q] = a.mapping[t < n ? t : n - 1];   // uniform
         }
     };
     for (int c0 = 0; c0 < steps; c0 += kSteps) {
@@ -242,7 +242,250 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepareArgs a, int32_
     }
 }
 
+// ---- Several workgroups, for batches of at least kMultiMin tokens.  The
+// batch is cut into G contiguous chunks, one per workgroup, and the sort
+// runs in two launches:
+//   rank: each workgroup ranks its chunk as above (per-wave slices, match
+//         masks) and turns the ranks into ranks within the chunk; it writes
+//         (key, rank) per token and its chunk's count per key to scratch,
+//         and whether the chunk holds a valid id or an id out of range;
+//   place: every workgroup adds, per key, the counts of the chunks before
+//         its own and scans the keys' totals (the same scan on every
+//         workgroup), so a token's position is
+//           start[key] + counts of key in earlier chunks + rank in chunk;
+//         workgroup 0 also writes the distinct ids, counts, segment starts,
+//         flag and status.
+// The stable order is that of the single workgroup: chunks, then slices,
+// then lanes, all in token order.  Scratch: the library-owned stream-K slot
+// area (N + G * (max_loras + 2) words).
+constexpr int kMultiMin = 4096;
+constexpr int kMultiWork = 64;
+constexpr int kMultiMaxGroups = 64;
+
+__device__ __forceinline__ int *multi_packed(int32_t *scratch) { return scratch; }
+__device__ __forceinline__ int *multi_hist(int32_t *scratch, int n, int nkeys, int g) {
+    return scratch + n + g * (nkeys + 1);
+}
+
+__global__ __launch_bounds__(kThreads) void prepare_rank_kernel(PrepareArgs a, int32_t *scratch, int chunk) {
+    __shared__ __attribute__((aligned(16))) int s_cnt[kWaves][kMaxKeys];
+    __shared__ int s_any, s_bad;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int n = a.num_tokens, g = blockIdx.x;
+    const int nkeys = a.max_loras + 1;
+    const int nbits = 32 - __clz(nkeys - 1);
+    const int c0 = g * chunk, len = min(chunk, n - c0);
+    const int steps = (len + kThreads - 1) / kThreads;
+    const int slice = steps * kWave;
+    const int t0 = c0 + wave * slice, tend = c0 + len;
+    const bool in_regs = steps <= kSteps;
+    int *packed_out = multi_packed(scratch);
+
+    for (int k = tid; k < kWaves * nkeys; k += kThreads) s_cnt[k / nkeys][k % nkeys] = 0;
+    if (tid == 0) {
+        s_any = 0;
+        s_bad = 0;
+    }
+    __syncthreads();
+
+    int packed[kSteps];
+    int ids[kSteps];
+    bool any = false, bad = false;
+    for (int cs = 0; cs < steps; cs += kSteps) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            const int t = t0 + (cs + q) * kWave + lane;
+            if (cs + q < steps) ids[q] = a.mapping[t < tend ? t : tend - 1];   // uniform
+        }
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            if (cs + q >= steps) break;   // uniform
+            const int t = t0 + (cs + q) * kWave + lane;
+            const bool valid = t < tend;
+            int id = valid ? ids[q] : -1;
+            if (id < -1 || id >= a.max_loras) {
+                bad = true;
+                id = -1;
+            }
+            const int key = id + 1;
+            any |= valid && id != -1;
+            const int k0 = __builtin_amdgcn_readfirstlane(key);
+            const uint64_t m = ballot(valid && key != k0) == 0 ? ballot(valid) : match_key(key, valid, nbits);
+            const bool leader = valid && (m & lanemask_lt()) == 0;
+            const int rank = s_cnt[wave][key] + __popcll(m & lanemask_lt());
+            packed[q] = (key << kRankBits) | rank;
+            if (leader) s_cnt[wave][key] += __popcll(m);
+        }
+        if (!in_regs) {
+#pragma unroll
+            for (int q = 0; q < kSteps; ++q) {
+                const int t = t0 + (cs + q) * kWave + lane;
+                if (cs + q < steps && t < tend) packed_out[t] = packed[q];
+            }
+        }
+    }
+    if (ballot(any) && lane == 0) atomicOr(&s_any, 1);
+    if (ballot(bad) && lane == 0) atomicOr(&s_bad, 1);
+    __syncthreads();
+    // per key: the chunk's count, and each wave's base within the chunk
+    int *hist = multi_hist(scratch, n, nkeys, g);
+    if (tid < nkeys) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = s_cnt[w][tid];
+            s_cnt[w][tid] = run;
+            run += c;
+        }
+        hist[tid] = run;
+    }
+    if (tid == 0) hist[nkeys] = s_any | (s_bad << 1);
+    __syncthreads();
+    // ranks within the chunk
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            const int t = t0 + q * kWave + lane;
+            if (q < steps && t < tend) {
+                const int key = (int)((unsigned)packed[q] >> kRankBits);
+                packed_out[t] = packed[q] + s_cnt[wave][key];
+            }
+        }
+    } else {
+        for (int q = 0; q < steps; ++q) {
+            const int t = t0 + q * kWave + lane;
+            if (t < tend) {
+                const int v = packed_out[t];
+                packed_out[t] = v + s_cnt[wave][(int)((unsigned)v >> kRankBits)];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void prepare_place_kernel(PrepareArgs a, int32_t *scratch, int chunk, int groups,
+                                                                 int32_t *sk_counters, int sk_words) {
+    if ((int)blockIdx.x >= groups) {
+        // the remaining workgroups clear the fused calls' and the stream-K
+        // shrink's counters (the clearing below indexes from workgroup 1)
+        PrepareArgs c = a;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int stride = (gridDim.x - groups) * kThreads;
+        const int first = (blockIdx.x - groups) * kThreads + threadIdx.x;
+        for (int k = first; k < c.sync_tiles * kSyncGroups; k += stride) {
+            const int tile = k / kSyncGroups, w = k % kSyncGroups;
+            const int word = w == 0 ? kFusedPastWait : w == 1 ? kFusedPartsDone : kFusedFlags + 4 * (w - 2);
+            *reinterpret_cast<u32x4 *>(c.sync + kFusedTileWords * tile + word) = z;
+        }
+        for (int k = first; k < c.acc_floats / 4; k += stride) reinterpret_cast<u32x4 *>(c.acc)[k] = z;
+        for (int k = first; k < sk_words / 4; k += stride) reinterpret_cast<u32x4 *>(sk_counters)[k] = z;
+        return;
+    }
+    __shared__ int s_base[kMaxKeys];
+    __shared__ int s_wa[kWaves], s_wb[kWaves];
+    __shared__ int s_flags;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int n = a.num_tokens, g = blockIdx.x;
+    const int nkeys = a.max_loras + 1;
+    const int c0 = g * chunk, tend = min(c0 + chunk, n);
+    const int *packed = multi_packed(scratch);
+    // this thread's first token, loaded now so that its round trip overlaps
+    // the counts' (a chunk holds at most kThreads tokens when g < kMultiMaxGroups)
+    const int v0 = c0 + tid < tend ? packed[c0 + tid] : 0;
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+    if (tid < groups) {
+        const int f = multi_hist(scratch, n, nkeys, tid)[nkeys];
+        if (f) atomicOr(&s_flags, f);
+    }
+    // per key: counts in the chunks before this one, and in all chunks
+    // (16 loads in flight at a time)
+    int before = 0, c = 0;
+    if (tid < nkeys) {
+        for (int k0 = 0; k0 < groups; k0 += 16) {
+            int h[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) h[q] = k0 + q < groups ? multi_hist(scratch, n, nkeys, k0 + q)[tid] : 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                before += k0 + q < g ? h[q] : 0;
+                c += h[q];
+            }
+        }
+    }
+    __syncthreads();
+    const bool any = s_flags & 1, bad = (s_flags >> 1) & 1;
+    if (!any) {   // the pages' early return: reset values and the flag only
+        if (g == 0) {
+            if (tid == 0) {
+                *a.no_lora = 1;
+                *a.status = bad ? LORA_ERR_ID_RANGE : 0;
+            }
+            for (int k = tid; k < nkeys; k += kThreads) {
+                a.active_ids[k] = -1;
+                a.counts[k] = 0;
+            }
+            for (int k = tid; k < nkeys + 1; k += kThreads) a.start_loc[k] = 0;
+        }
+        return;
+    }
+    const int ne = c > 0 ? 1 : 0;
+    const int ic = wave_inclusive_scan(c), ine = wave_inclusive_scan(ne);
+    if (lane == kWave - 1) {
+        s_wa[wave] = ic;
+        s_wb[wave] = ine;
+    }
+    __syncthreads();
+    int start = ic - c, slot = ine - ne, n_active = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int va = s_wa[w], vb = s_wb[w];
+        start += w < wave ? va : 0;
+        slot += w < wave ? vb : 0;
+        n_active += vb;
+    }
+    if (tid < nkeys) s_base[tid] = start + before;
+    if (g == 0) {
+        if (tid == 0) {
+            *a.no_lora = 0;
+            *a.status = bad ? LORA_ERR_ID_RANGE : 0;
+        }
+        if (ne) {
+            a.active_ids[slot] = tid - 1;
+            a.counts[slot] = c;
+            a.start_loc[slot + 1] = start + c;
+        }
+        for (int k = tid; k < nkeys; k += kThreads) {
+            if (k >= n_active) {
+                a.active_ids[k] = -1;
+                a.counts[k] = 0;
+            }
+        }
+        for (int k = tid; k < nkeys + 1; k += kThreads)
+            if (k == 0 || k > n_active) a.start_loc[k] = 0;
+    }
+    __syncthreads();
+    for (int t = c0 + tid; t < tend; t += kThreads) {
+        const int v = t == c0 + tid ? v0 : packed[t];
+        const int key = (int)((unsigned)v >> kRankBits), rank = v & kRankMask;
+        const int pos = s_base[key] + rank;
+        if ((unsigned)pos < (unsigned)n) a.sorted[pos] = t;
+        a.mapping_copy[t] = key - 1;
+    }
+}
+
 }  // namespace
+
+// The single workgroup's ranking takes about (64-token steps per wave) x
+// (key bits + 2) units of work: several workgroups pay for a second launch
+// once that passes kMultiWork (about 4 us of ranking; measured crossover).
+bool multi_prepare(int n, int max_loras) {
+    const int nkeys = max_loras + 1;
+    const int nbits = nkeys > 1 ? 32 - __builtin_clz((unsigned)(nkeys - 1)) : 0;
+    const long steps = (n + kThreads - 1) / kThreads;
+    return n >= kMultiMin && steps * (nbits + 2) >= kMultiWork;
+}
+
+int prepare_launches(int n, int max_loras) { return multi_prepare(n, max_loras) ? 2 : 1; }
 
 // One sorting workgroup, plus workgroups that clear the fused call's area
 // (about 4 16-byte stores per thread) when the batch can use it.
@@ -251,6 +494,20 @@ hipError_t launch_prepare(const PrepareArgs &a, int32_t *sk_counters, int sk_wor
     const long groups = (long)a.sync_tiles * kSyncGroups + a.acc_floats / 4 + sk_words / 4;
     long clear = (groups + 4L * kThreads - 1) / (4L * kThreads);
     if (clear > 64) clear = 64;
+    if (multi_prepare(a.num_tokens, a.max_loras) && sk_counters) {
+        // several sorting workgroups; scratch in the stream-K slot area
+        int32_t *scratch = sk_counters + kSkCounterWords;
+        int g = (a.num_tokens + kThreads - 1) / kThreads;
+        if (g > kMultiMaxGroups) g = kMultiMaxGroups;
+        const int chunk = (a.num_tokens + g - 1) / g;
+        g = (a.num_tokens + chunk - 1) / chunk;
+        hipLaunchKernelGGL(prepare_rank_kernel, dim3((unsigned)g), dim3(kThreads), 0, s, a, scratch, chunk);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(prepare_place_kernel, dim3((unsigned)(g + clear)), dim3(kThreads), 0, s, a, scratch, chunk, g,
+                           sk_counters, sk_words);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)(1 + clear)), dim3(kThreads), 0, s, a, sk_counters, sk_words);
     return hipGetLastError();
 }

@@ -38,7 +38,15 @@ def test_launch_count_query(monkeypatch):
     assert q(256, 32, 4096, 1, 64, False) == 1 and q(256, 32, 4096, 1, 72, False) in sep
     assert q(256, 32, 4096, 3, 32, False) in sep
     assert q(23 * 1024, 1023, 4096, 1, 8, False) == 1 and q(23 * 1024 + 1, 1023, 4096, 1, 8, False) in sep
-    assert q(16384, 128, 8192, 3, 128, False) == 2 and q(16384, 128, 8192, 3, 128, True) == 3
+    # large batches with wide ids are prepared in two launches (rank, then place)
+    p = sgl.lora_prepare_meta_launches
+    assert p(0, 128) == 1 and p(4095, 1023) == 1 and p(4096, 1023) == 1 and p(8192, 1023) == 2 and p(2097152, 1) == 2
+    assert p(8192, 8) == 1 and p(8192, 128) == 2 and p(16384, 128) == 2 and p(4096, 64) == 1
+    for bad in [(-1, 8), (8, 0), (8, 1024)]:
+        with pytest.raises(sgl.LoraError):
+            p(*bad)
+    assert q(16384, 128, 8192, 3, 128, False) == 2 and q(16384, 128, 8192, 3, 128, True) == 4
+    assert q(8192, 8, 4096, 3, 64, True) == 3
     # the stream-K shrink (batches of 1024 tokens or more) adds its parts up without atomics
     assert q(4096, 64, 14336, 1, 32, False) == 2 and q(4096, 64, 14336, 1, 32, True) == 3
     # without it, a split-K shrink into a fresh buffer zeroes the active rows first (Zipf's down layer)
@@ -93,11 +101,13 @@ def test_algorithmic_bytes_formulas():
 def test_plan_merges_and_replays():
     p = bench.Plan()
     p.workload, p.phase = "w", "timed"
-    p.replay([("preplinear0", 3), ("linear1", 2)], 2)
-    p.add("expand0", 1, times=4)
-    assert p.calls == [["w", "timed", "preplinear0", 3, 1], ["w", "timed", "linear1", 2, 1],
-                       ["w", "timed", "preplinear0", 3, 1], ["w", "timed", "linear1", 2, 1],
-                       ["w", "timed", "expand0", 1, 4]]
+    A, B = ["prepare", "shrink", "expand"], ["shrink", "expand"]
+    p.replay([("preplinear0", A), ("linear1", B)], 2)
+    p.add("expand0", ["expand"], times=4)
+    p.add("expand0", ["expand"])
+    assert p.calls == [["w", "timed", "preplinear0", A, 1], ["w", "timed", "linear1", B, 1],
+                       ["w", "timed", "preplinear0", A, 1], ["w", "timed", "linear1", B, 1],
+                       ["w", "timed", "expand0", ["expand"], 5]]
 
 
 def _write_trace(path, names_durations):
@@ -113,10 +123,12 @@ def _write_trace(path, names_durations):
 def test_summarize_trace_matches_plan(tmp_path):
     """Library dispatches (foreign kernels ignored) matched one by one with the
     plan; per workload, phase, call and kernel averages."""
-    plan = {"calls": [["zipf", "warmup", "preplinear0", 3, 1],
-                      ["zipf", "timed", "preplinear0", 3, 1], ["zipf", "timed", "linear1", 3, 1],
-                      ["zipf", "timed", "preplinear0", 3, 1], ["zipf", "timed", "linear1", 3, 1],
-                      ["decode", "per_call", "preplinear0", 1, 2]]}
+    A, B = ["prepare", "shrink", "expand"], ["zero", "shrink", "expand"]
+    plan = {"calls": [["zipf", "warmup", "preplinear0", A, 1],
+                      ["zipf", "timed", "preplinear0", A, 1], ["zipf", "timed", "linear1", B, 1],
+                      ["zipf", "timed", "preplinear0", A, 1], ["zipf", "timed", "linear1", B, 1],
+                      ["decode", "per_call", "preplinear0", ["one_launch"], 2],
+                      ["large", "timed", "prepare", ["prepare_rank", "prepare_place"], 1]]}
     json.dump(plan, open(tmp_path / "plan.json", "w"))
     P, Z = "void lora::prepare_kernel(lora::PrepareArgs)", "void lora::zero_rows_kernel(lora::ShrinkArgs)"
     S0, S1 = "void lora::shrink_lds_kernel<4, 2, 2, 4>(lora::ShrinkArgs)", "void lora::shrink_lds_kernel<2,2,2,4>(x)"
@@ -125,18 +137,21 @@ def test_summarize_trace_matches_plan(tmp_path):
     rows = [(P, 7), (S0, 20), (E, 100), ("torch_fill", 3),
             (P, 6), (S0, 24), (E, 110), (Z, 2), (S1, 40), (E, 30),
             (P, 6), (S0, 26), (E, 130), (Z, 2), (S1, 44), (E, 34),
-            (LM, 13000), (LM, 15000)]
+            (LM, 13000), (LM, 15000),
+            ("void lora::prepare_rank_kernel(lora::PrepareArgs, int*, int)", 3000),
+            ("void lora::prepare_place_kernel(lora::PrepareArgs, int*, int, int, int*, int)", 2000)]
     _write_trace(tmp_path / "t.csv", rows)
     out = bench.summarize_trace(str(tmp_path / "t.csv"), str(tmp_path / "plan.json"), str(tmp_path / "o.md"), "cmd")
     assert out["zipf/timed/preplinear0/shrink0"] == 0.025 and out["zipf/timed/preplinear0/expand0"] == 0.12
     assert out["zipf/timed/linear1/expand1"] == 0.032 and out["zipf/timed/linear1/zero1"] == 0.002
     assert out["zipf/timed/preplinear0/prepare"] == 0.006
     assert out["decode/per_call/preplinear0/one_launch0"] == 14.0
+    assert out["large/timed/prepare/prepare_rank"] == 3.0 and out["large/timed/prepare/prepare_place"] == 2.0
     assert not any(k.startswith("zipf/warmup") for k in out)
 
 
 def test_summarize_trace_rejects_a_mismatch(tmp_path):
-    json.dump({"calls": [["w", "timed", "shrink0", 1, 1]]}, open(tmp_path / "plan.json", "w"))
+    json.dump({"calls": [["w", "timed", "shrink0", ["shrink"], 1]]}, open(tmp_path / "plan.json", "w"))
     _write_trace(tmp_path / "t.csv", [("void lora::expand_kernel<1,1,true,true>(a)", 5)])
     with pytest.raises(SystemExit):
         bench.summarize_trace(str(tmp_path / "t.csv"), str(tmp_path / "plan.json"), str(tmp_path / "o.md"), "c")
