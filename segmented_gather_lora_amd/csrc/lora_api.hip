@@ -325,6 +325,7 @@ ExpandTuning expand_tuning() {
     if (cfg.tile_tokens % 16) cfg.tile_tokens = 0;
     cfg.grid_cap = env_int("LORA_EXPAND_GRID");
     cfg.run_blocks = env_int("LORA_EXPAND_RUN");
+    cfg.share = env_int("LORA_EXPAND_SHARE");
     return cfg;
 }
 

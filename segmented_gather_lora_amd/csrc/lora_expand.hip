@@ -76,20 +76,9 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     const int rank = a.rank;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 
-    const UnitWalker walk(total * a.runs);
-    for (int jj = walk.first;; jj += walk.stride) {
-        const int u = walk.unit(jj);
-        if (u < 0) break;
-        const int run = u % a.runs;
-        const TileRef tr = lookup_tile(smem, nslots, u / a.runs);
-        int i = 0;
-#pragma unroll
-        for (int s = 1; s < LORA_MAX_SLICES; ++s)
-            if (s < a.num_slices && run >= a.run_begin[s]) i = s;
+    // One piece of work: token tile `tr`, column blocks [cb0, cb0 + ncb) of slice i.
+    auto run_piece = [&](const TileRef &tr, int i, int cb0, int ncb) {
         const int width = select_slice(a.width, i);
-        const int blocks_i = (width + kBlockCols - 1) / kBlockCols;
-        const int cb0 = (run - select_slice(a.run_begin, i)) * a.run_blocks;
-        const int ncb = min(a.run_blocks, blocks_i - cb0);
         const int pbase = tr.tile * kUnitTokens;
         const float *bufs = a.buf + (int64_t)i * a.num_tokens * rank;
 
@@ -243,7 +232,51 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
                 }
             }
         }
-        __syncthreads();   // the staged rows are rewritten by the next unit
+        __syncthreads();   // the staged rows are rewritten by the next piece
+    };
+    // the slice of (single-block or run) index b of a tile
+    auto slice_of = [&](int b) {
+        int i = 0;
+#pragma unroll
+        for (int s = 1; s < LORA_MAX_SLICES; ++s)
+            if (s < a.num_slices && b >= a.run_begin[s]) i = s;
+        return i;
+    };
+
+    // The pieces of this workgroup.  With a.share: equal shares of the (tile,
+    // column block) list (runs are single blocks then), in XCD order, cut
+    // anywhere, since column blocks need no combining, so every workgroup
+    // gets the same number of blocks to within one.  Otherwise units of
+    // a.run_blocks blocks of one slice, walked in one chunk per XCD.
+    const long W = (long)total * a.runs;
+    const int G = gridDim.x;
+    const int share_id = (int)(blockIdx.x % kNumXcd) * (G / kNumXcd) + (int)(blockIdx.x / kNumXcd);
+    const long end = a.share ? W * (share_id + 1) / G : 0;
+    long cur = a.share ? W * share_id / G : 0;
+    const UnitWalker walk(a.share ? 0 : (int)W);
+    for (int jj = walk.first;;) {
+        int t, i, cb0, ncb;
+        if (a.share) {
+            if (cur >= end) break;
+            t = (int)(cur / a.runs);
+            const int b = (int)(cur - (long)t * a.runs);
+            i = slice_of(b);
+            cb0 = b - select_slice(a.run_begin, i);
+            const int blocks_i = (select_slice(a.width, i) + kBlockCols - 1) / kBlockCols;
+            ncb = (int)min((long)(blocks_i - cb0), end - cur);
+            cur += ncb;
+        } else {
+            const int u = walk.unit(jj);
+            if (u < 0) break;
+            jj += walk.stride;
+            t = u / a.runs;
+            const int run = u % a.runs;
+            i = slice_of(run);
+            cb0 = (run - select_slice(a.run_begin, i)) * a.run_blocks;
+            const int blocks_i = (select_slice(a.width, i) + kBlockCols - 1) / kBlockCols;
+            ncb = min(a.run_blocks, blocks_i - cb0);
+        }
+        run_piece(lookup_tile(smem, nslots, t), i, cb0, ncb);
     }
 }
 
@@ -326,13 +359,29 @@ hipError_t launch_expand(const ExpandArgs &in, const ExpandTuning &cfg, hipStrea
         r = avg < 16 ? 16 : 4;
         while (r > 1 && tiles_upper * count_runs(r) < kMinUnits) r /= 2;
     }
+    // Shares of the (tile, column block) list instead of units of r blocks
+    // (LORA_EXPAND_SHARE=1 forces it, 2 turns it off), for ranks above 64:
+    // there a unit is long (each block moves 16 KB of weights per wave) and
+    // the uneven count of units per workgroup costs most (measured: large
+    // 221 -> 200 us; no gain on the rank-64 prefill shape, a loss on the
+    // rank-16 and rank-32 shapes).
+    a.share = cfg.share == 1 || (cfg.share == 0 && cfg.run_blocks <= 0 && r > 1 && a.rank > 64);
+    if (a.share) r = 1;
     a.run_blocks = r;
     a.runs = (int)count_runs(r);
-    const ExpandFn fn = pick(ks, tt, add, r == 1);
+    const ExpandFn fn = pick(ks, tt, add, r == 1 && !a.share);
     const long units_upper = tiles_upper * a.runs;
     a.num_units = (int)units_upper;
-    const long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : 2048,
-                                      reinterpret_cast<const void *>(fn), kThreads, lds);
+    long grid = persistent_grid(units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : 2048,
+                                reinterpret_cast<const void *>(fn), kThreads, lds);
+    if (a.share && cfg.grid_cap <= 0) {
+        // every resident workgroup, as long as each gets a few blocks
+        long res = resident_grid(reinterpret_cast<const void *>(fn), kThreads, lds);
+        const long by_work = units_upper / 4;
+        if (res > by_work) res = by_work;
+        grid = res / kNumXcd * kNumXcd;
+        if (grid < kNumXcd) grid = kNumXcd;
+    }
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -361,6 +361,7 @@ struct ExpandArgs {
     int32_t tile_tokens;  // tokens per work unit (multiple of 16)
     int32_t num_units;
     int32_t add_inputs;
+    int32_t share;        // 1: workgroups take equal shares of the (tile, column block) list
 };
 
 // Launch-geometry overrides (0 = automatic), read from the environment by the
@@ -379,6 +380,7 @@ struct ExpandTuning {
     int tile_tokens;       // 16, 32 or 64
     int grid_cap;
     int run_blocks;        // column blocks per unit
+    int share;             // 0 automatic, 1 shares of the block list, 2 units of run_blocks
 };
 
 // Workgroups of kernel `fn` the device holds at once (host side, cached).

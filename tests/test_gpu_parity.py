@@ -251,6 +251,23 @@ def test_expand_run_variants(run, tt, rank, add_inputs, monkeypatch):
     H.run_and_check(wl, add_inputs=add_inputs, offset_start=16, ldy_extra=8)
 
 
+@pytest.mark.parametrize("grid", [0, 8, 2048])
+@pytest.mark.parametrize("tt,rank", [(16, 16), (64, 64), (64, 128)])
+@pytest.mark.parametrize("add_inputs", [True, False])
+def test_expand_share_variants(grid, tt, rank, add_inputs, monkeypatch):
+    """Equal shares of the (tile, column block) list: shares that start and
+    end inside a slice or a tile, ragged slice widths, bias, an offset; with
+    few workgroups (long shares) and more workgroups than blocks (empty ones)."""
+    monkeypatch.setenv("LORA_EXPAND_SHARE", "1")
+    monkeypatch.setenv("LORA_EXPAND_TILE_TOKENS", str(tt))
+    if grid:
+        monkeypatch.setenv("LORA_EXPAND_GRID", str(grid))
+    wl = workloads.random_case(170 + tt + rank, 300, 64, (1800, 264, 8, 776), rank, 6, bias=True,
+                               neg_fraction=0.15)
+    print("expand share", grid, tt, rank, add_inputs, flush=True)
+    H.run_and_check(wl, add_inputs=add_inputs, offset_start=16, ldy_extra=8)
+
+
 def _gpu_outputs(wl, meta, buf0=None):
     sgl = H.lib()
     L = wl.layers[0]
