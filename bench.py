@@ -785,8 +785,9 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
 def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     """Time every tiling of one kernel on a full-size workload (the library's
     tuning overrides; each changes the tiling only, never the result): the
-    LDS-staged shrink configurations x K splits, or the expand tile sizes x
-    column-block run lengths.  Cold inputs, HIP-graph replays of one call."""
+    LDS-staged shrink configurations x K splits and their stream-K forms, or
+    the expand tile sizes x column-block run lengths and the share walk.
+    Cold inputs, HIP-graph replays of one call."""
     import torch
     import workloads
     if wl is None:
@@ -800,15 +801,19 @@ def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     torch.cuda.synchronize()
     n = max(8, rotate)
     env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_SHRINK_SK",
-           "LORA_EXPAND_TILE_TOKENS", "LORA_EXPAND_RUN")
+           "LORA_EXPAND_TILE_TOKENS", "LORA_EXPAND_RUN", "LORA_EXPAND_SHARE")
     if grid is not None:
         grid = [dict(g) for g in grid]
     elif what == "shrink":
-        grid = [dict(LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
+        # units of every staged configuration with 1-4 K chunks, and the stream-K form of each
+        grid = [dict(LORA_SHRINK_SK="1", LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
                 for c in range(1, 20) for k in (1, 2, 3, 4)]
+        grid += [dict(LORA_SHRINK_SK="2", LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c)) for c in range(1, 20)]
     else:
-        grid = [dict(LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
+        # units of a run of column blocks, and equal shares of the block list
+        grid = [dict(LORA_EXPAND_SHARE="2", LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
                 for t in (16, 32, 64) for r in (1, 2, 4, 8, 16)]
+        grid += [dict(LORA_EXPAND_SHARE="1", LORA_EXPAND_TILE_TOKENS=str(t)) for t in (16, 32, 64)]
     if {} not in grid:
         grid.append({})   # the automatic choice
     command = "python bench.py " + " ".join(shlex.quote(a) for a in sys.argv[1:])
