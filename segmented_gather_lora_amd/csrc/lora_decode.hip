@@ -4,10 +4,10 @@
 // The tile-major one-launch kernel can only start reading weights once the
 // batch is sorted, because a workgroup learns which LoRA its tile holds from
 // the sort.  Here workgroup L + max_loras * idx serves LoRA id L in role idx,
-// so it issues its weight loads as it starts (right after the ids, which
-// therefore arrive first), and needs no sort: it picks out its own tokens
-// with one ballot per 64 tokens, in batch order (the order the stable sort
-// gives them within the segment).
+// so its weight addresses are known at entry: a shrink part requests its
+// weights with its ids, an expander as soon as its ids are in.  It needs no
+// sort: it picks out its own tokens with one ballot per 64 tokens, in batch
+// order (the order the stable sort gives them within the segment).
 //
 // Roles of id L:
 //   - idx < parts: shrink part idx -- K chunk idx of all S*r weight rows, for
@@ -62,9 +62,13 @@ __device__ __forceinline__ void load_ids(const int32_t *mapping, int n, Ids &ids
     ids.steps = (n + kThreads - 1) / kThreads;
     ids.t0 = wave_id() * ids.steps * kWave;
 #pragma unroll
-    for (int q = 0; q < kFilterSteps; ++q) {   // addresses clamped: no branch before the loads
+    for (int q = 0; q < kFilterSteps; ++q) {   // addresses clamped
+        // only the wave's own steps: every workgroup of the launch reads
+        // these few lines, and clamped loads past the batch would pile onto
+        // the one holding its last id
         const int t = ids.t0 + q * kWave + lane_id();
-        ids.v[q] = mapping[t < n ? t : n - 1];
+        ids.v[q] = 0;
+        if (q < ids.steps) ids.v[q] = mapping[t < n ? t : n - 1];   // uniform
     }
 }
 
@@ -381,10 +385,14 @@ void lora_major_kernel(FusedArgs f) {
         braw = bk.bptr ? *reinterpret_cast<const u32x2 *>(bk.bptr + (int64_t)L * bk.width + bk.grp)
                        : u32x2{0u, 0u};
     };
+    // the weights are requested once the ids are in: loads return in order,
+    // so weight loads issued first would hold up this compute unit's later
+    // id loads (the shrink parts' among them); an id with no tokens then
+    // reads none
     Block bk = block_at(e0);
-    load_weights(bk);
 
     const int cnt = pick_tokens<true>(ids, n, mine, s_list, s_wcnt);
+    if (cnt > 0) load_weights(bk);
     auto token_at = [&](int pidx) { return s_list[pidx < cnt ? pidx : cnt - 1]; };
     // y rows of tile `t` for the current block (no dependence on buf)
     u32x2 yv[4];

@@ -41,15 +41,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kWaveCols = 64;
 constexpr int kBlockCols = kWaves * kWaveCols;
 
-template <typename T, int N>
-__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
-    T r = p[0];
-#pragma unroll
-    for (int s = 1; s < N; ++s)
-        if (i == s) r = p[s];
-    return r;
-}
-
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }

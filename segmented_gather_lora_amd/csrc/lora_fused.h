@@ -38,15 +38,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 __device__ __forceinline__ int clamp_group(int c, int width) { return c < width ? c : width - 4; }
 
-template <typename T, int N>
-__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
-    T r = p[0];
-#pragma unroll
-    for (int s = 1; s < N; ++s)
-        if (i == s) r = p[s];
-    return r;
-}
-
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 __device__ __forceinline__ void reset_tile(int32_t *words, int parts) {

@@ -76,8 +76,12 @@ __device__ int prepare_in_lds(const PrepareArgs &p, int tile_tokens, int *smem, 
     int ids[kSteps];
 #pragma unroll
     for (int q = 0; q < kSteps; ++q) {   // one round trip (addresses clamped)
+        // only the wave's own steps: every workgroup of the launch reads
+        // these few lines, and clamped loads past the batch would pile onto
+        // the one holding its last id
         const int t = t0 + q * kWave + lane;
-        ids[q] = p.mapping[t < n ? t : n - 1];
+        ids[q] = 0;
+        if (q < steps) ids[q] = p.mapping[t < n ? t : n - 1];   // uniform
     }
     __syncthreads();
 

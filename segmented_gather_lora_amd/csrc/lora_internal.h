@@ -98,23 +98,38 @@ __device__ __forceinline__ void prefetch_kernargs() {
     else LORA_KA_ASM(LORA_KA_L11);
 }
 
+// Entry i of a per-slice table in the argument block; i is uniform or nearly
+// so, and each entry is compared rather than indexed.
+template <typename T, int N>
+__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
+    T r = p[0];
+#pragma unroll
+    for (int s = 1; s < N; ++s)
+        if (i == s) r = p[s];
+    return r;
+}
+
 // Pointer i of a kernel-argument pointer table, where i differs between
 // lanes.  Every entry is taken through readfirstlane, so the table is read
 // with scalar loads and the pick is a per-lane select; a plain p[i] would
 // become a per-lane gather from the argument block on the vector memory path,
-// whose wait also holds up every load issued before it.
+// whose wait also holds up every load issued before it.  The entries are
+// rebuilt as global-memory pointers: rebuilt as plain (generic) pointers they
+// would make flat loads, which count on the LDS counter as well, so that
+// every LDS wait after them (the next barrier) would wait for them too.
 template <typename T, int N>
 __device__ __forceinline__ T *lane_slice_ptr(T *const (&p)[N], int i) {
-    T *r = nullptr;
+    typedef __attribute__((address_space(1))) T GT;
+    GT *r = nullptr;
 #pragma unroll
     for (int s = 0; s < N; ++s) {
         const uint64_t v = reinterpret_cast<uint64_t>(p[s]);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-        T *ps = reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+        GT *ps = (GT *)(((uint64_t)hi << 32) | lo);
         r = (s == 0 || i == s) ? ps : r;
     }
-    return r;
+    return (T *)r;
 }
 
 // ---------------------------------------------------------------- bf16

@@ -35,15 +35,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T, int N>
-__device__ __forceinline__ T select_slice(const T (&p)[N], int i) {
-    T r = p[0];
-#pragma unroll
-    for (int s = 1; s < N; ++s)
-        if (i == s) r = p[s];
-    return r;
-}
-
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // Loads of one 64-wide K step: 16 elements of each row at kk (clamped to the
