@@ -782,6 +782,10 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     return rec
 
 
+# LDS-staged shrink configurations the library defines (LORA_SHRINK_STAGED=1..)
+STAGED_CFGS = 27
+
+
 def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     """Time every tiling of one kernel on a full-size workload (the library's
     tuning overrides; each changes the tiling only, never the result): the
@@ -807,8 +811,9 @@ def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     elif what == "shrink":
         # units of every staged configuration with 1-4 K chunks, and the stream-K form of each
         grid = [dict(LORA_SHRINK_SK="1", LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c), LORA_SHRINK_KSPLIT=str(k))
-                for c in range(1, 20) for k in (1, 2, 3, 4)]
-        grid += [dict(LORA_SHRINK_SK="2", LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c)) for c in range(1, 20)]
+                for c in range(1, STAGED_CFGS + 1) for k in (1, 2, 3, 4)]
+        grid += [dict(LORA_SHRINK_SK="2", LORA_SHRINK_VARIANT="3", LORA_SHRINK_STAGED=str(c))
+                 for c in range(1, STAGED_CFGS + 1)]
     else:
         # units of a run of column blocks, and equal shares of the block list
         grid = [dict(LORA_EXPAND_SHARE="2", LORA_EXPAND_TILE_TOKENS=str(t), LORA_EXPAND_RUN=str(r))
