@@ -439,160 +439,8 @@ struct Staged : TileLayout<NT, MR, WR> {
     }
 };
 
-// The same piece of work with only the token rows staged through LDS: each
-// wave owns its weight rows (WR = 4: a row group of its own), so they gain
-// nothing from LDS and go straight from memory into the wave's MFMA operand
-// registers, D steps ahead.  LDS then holds D steps of the tile's token rows
-// alone, so a tile can cover every weight row of the layer (token rows are
-// read once per tile instead of once per row block) and still keep D steps in
-// flight.  Lane (n16, g) loads 16-byte pieces 4h + g (h = 0, 1) of its weight
-// row in each 128-byte K step: one instruction reads 64 contiguous bytes of
-// each of 16 rows, and K half h of the step is the MFMA's natural 32-wide K
-// block.  Token row pieces are read from LDS at the matching positions (the
-// XOR swizzle of the staged kernel).
-template <int NT, int MR, int WR, int D>
-struct XStaged : TileLayout<NT, MR, WR> {
-    using L = TileLayout<NT, MR, WR>;
-    using typename L::Acc;
-    using L::BT;
-    using L::BR;
-    using L::MT;
-    using L::NTW;
-    static constexpr int NSTAGE = D;
-    static constexpr int INSTR = BT / 32;            // token row loads per wave per step (8 rows each)
-    static constexpr int PER_STEP = INSTR + 2 * MT;  // vector memory instructions per wave per step
-    static constexpr bool SPLIT_H = MT * NTW >= 40;
-    static_assert(BT % 32 == 0, "token rows per wave");
-    static_assert((D - 1) * PER_STEP < 64, "vmcnt range");
-    typedef unsigned char Stage[BT * 128];
-
-    __device__ __forceinline__ static Acc run(const ShrinkArgs &a, const TileRef &tr, int rb, int kbeg, int kend,
-                                              Stage *stage) {
-        Acc out;
-        floatx4 (&acc)[MT][NTW] = out.v;
-        const int lane = lane_id(), wave = wave_id();
-        const int wr = wave % WR, wc = wave / WR;
-        const int n16 = lane & 15, g = lane >> 4;
-        const int nsteps = (kend - kbeg + 63) / 64;
-
-        // token rows: instruction j of this wave covers tile rows
-        // (wave * INSTR + j) * 8 .. + 8, lane l row l / 8, global piece
-        // (l & 7) ^ (row & 7) landing in slot l & 7
-        const int chunk_k = 8 * ((lane & 7) ^ ((lane >> 3) & 7));
-        const uint16_t *xsrc[INSTR];
-#pragma unroll
-        for (int j = 0; j < INSTR; ++j) {
-            const int r = (wave * INSTR + j) * 8 + (lane >> 3);
-            int p = tr.tile * BT + r;
-            p = p < tr.seg_count ? p : tr.seg_count - 1;
-            int t = a.meta.sorted[tr.seg_start + p];
-            t = (unsigned)t < (unsigned)a.num_tokens ? t : 0;
-            xsrc[j] = a.x + (int64_t)t * a.ldx;
-        }
-        // weight rows: m-tile mt of this wave, row n16
-        const uint16_t *wsrc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            int row = rb * BR + (wr * MT + mt) * 16 + n16;
-            row = row < a.rows ? row : a.rows - 1;
-            const int i = row / a.rank, jr = row - i * a.rank;
-            wsrc[mt] = select_slice(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
-        }
-        u32x4 wv[D][MT][2];
-        // step `step` (past the end: the last one again) into stage d
-        auto issue = [&](int step, int d) {
-            const int k0 = kbeg + (step < nsteps ? step : nsteps - 1) * 64;
-#pragma unroll
-            for (int j = 0; j < INSTR; ++j) {
-                const int k = k0 + chunk_k;
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xsrc[j] + (k + 8 <= kend ? k : 0)),
-                                                 reinterpret_cast<void *>(&stage[d][(wave * INSTR + j) * 1024]),
-                                                 16, 0, 0);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k0 + 32 * h + 8 * g;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) wv[d][mt][h] = ld16(wsrc[mt] + (k + 8 <= kend ? k : 0));
-            }
-        };
-
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-        for (int st = 0; st < D - 1; ++st) issue(st, st);
-
-        for (int s0 = 0; s0 < nsteps; s0 += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int s = s0 + d;
-                if (s >= nsteps) break;   // uniform
-                issue(s + D - 1, (d + D - 1) % D);
-                // nothing moves across the wait: it counts exactly the
-                // instructions of the D - 1 steps issued after step s
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * PER_STEP));
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("" ::: "memory");
-                const unsigned char *sb = stage[d];
-                const bool mask = s == nsteps - 1 && ((kend - kbeg) & 63) != 0;
-                u32x4 xa[SPLIT_H ? 1 : 2][NTW];
-                auto read_half = [&](int h, int q) {
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) {
-                        const int r = (wc * NTW + nt) * 16 + n16;
-                        xa[q][nt] = lds_read16(sb + r * 128 + 16 * ((4 * h + g) ^ (r & 7)));
-                    }
-                };
-                if (!SPLIT_H) {
-                    read_half(0, 0);
-                    read_half(1, SPLIT_H ? 0 : 1);
-                    lds_wait();
-#pragma unroll
-                    for (int q = 0; q < (SPLIT_H ? 1 : 2); ++q)
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) after_wait(xa[q][nt]);
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int q = SPLIT_H ? 0 : h;
-                    if (SPLIT_H) {
-                        read_half(h, 0);
-                        lds_wait();
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) after_wait(xa[0][nt]);
-                    }
-                    u32x4 wq[MT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) wq[mt] = wv[d][mt][h];
-                    if (mask && kbeg + s * 64 + 32 * h + 8 * g + 8 > kend) {
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) xa[q][nt] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) wq[mt] = u32x4{0u, 0u, 0u, 0u};
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt)
-                            acc[mt][nt] = mfma16x16x32(as_bf16x8(wq[mt]), as_bf16x8(xa[q][nt]), acc[mt][nt]);
-                }
-                __builtin_amdgcn_s_barrier();   // every wave has read the stage: it may be refilled
-            }
-        }
-        // drain the loads issued past the end before the stages are reused
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_s_barrier();
-        return out;
-    }
-};
-
-// One kernel per piece runner S: the units (tile, row block, K chunk) are
-// walked in XCD-chunked order (UnitWalker).
+// The units (tile, row block, K chunk) walked in XCD-chunked order
+// (UnitWalker), each run by the piece runner S.
 template <class S>
 __device__ __forceinline__ void unit_walk(const ShrinkArgs &a, int *smem, int *s_wsum, typename S::Stage *stage) {
     const int nslots = a.meta.nslots;
@@ -620,15 +468,6 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
     extern __shared__ int smem[];
     __shared__ int s_wsum[kThreads / kWave];
     __shared__ __attribute__((aligned(1024))) typename S::Stage stage[STAGES];
-    unit_walk<S>(a, smem, s_wsum, stage);
-}
-
-template <int NT, int MR, int WR, int D>
-__global__ __launch_bounds__(kThreads) void shrink_xs_kernel(ShrinkArgs a) {
-    using S = XStaged<NT, MR, WR, D>;
-    extern __shared__ int smem[];
-    __shared__ int s_wsum[kThreads / kWave];
-    __shared__ __attribute__((aligned(1024))) typename S::Stage stage[D];
     unit_walk<S>(a, smem, s_wsum, stage);
 }
 
@@ -757,15 +596,6 @@ __global__ __launch_bounds__(kThreads) void shrink_sk_kernel(ShrinkArgs a, SkArg
     sk_walk<S>(a, sk, smem, s_wsum, stage);
 }
 
-template <int NT, int MR, int WR, int D>
-__global__ __launch_bounds__(kThreads) void shrink_xs_sk_kernel(ShrinkArgs a, SkArgs sk) {
-    using S = XStaged<NT, MR, WR, D>;
-    extern __shared__ int smem[];
-    __shared__ int s_wsum[kThreads / kWave];
-    __shared__ __attribute__((aligned(1024))) typename S::Stage stage[D];
-    sk_walk<S>(a, sk, smem, s_wsum, stage);
-}
-
 // Rows of the batch's active tokens set to zero, ahead of a split-K shrink
 // into a fresh buffer (its K chunks are added with atomics).  Rows of tokens
 // with id -1 are not touched.  Units are 16-token tiles.
@@ -853,15 +683,6 @@ const StagedCfg kStaged[] = {
     {2, 4, 4, 10, false, shrink_lds_kernel<2, 4, 4, 10>, shrink_sk_kernel<2, 4, 4, 10>},   // 16: 32 x 64, 10 stages
     {4, 4, 4, 8, false, shrink_lds_kernel<4, 4, 4, 8>, shrink_sk_kernel<4, 4, 4, 8>},     // 17: 64 x 64, 8 stages
     {2, 2, 2, 12, false, shrink_lds_kernel<2, 2, 2, 12>, shrink_sk_kernel<2, 2, 2, 12>},   // 18: 32 x 32, 12 stages
-    // token rows through LDS, weight rows straight into registers
-    {8, 24, 4, 3, false, shrink_xs_kernel<8, 24, 4, 3>, shrink_xs_sk_kernel<8, 24, 4, 3>},   // 19: 128 x 384, 3 steps
-    {8, 12, 4, 4, false, shrink_xs_kernel<8, 12, 4, 4>, shrink_xs_sk_kernel<8, 12, 4, 4>},   // 20: 128 x 192, 4 steps
-    {16, 12, 4, 3, false, shrink_xs_kernel<16, 12, 4, 3>, shrink_xs_sk_kernel<16, 12, 4, 3>},   // 21: 256 x 192, 3 steps
-    {8, 8, 4, 4, false, shrink_xs_kernel<8, 8, 4, 4>, shrink_xs_sk_kernel<8, 8, 4, 4>},       // 22: 128 x 128, 4 steps
-    {8, 4, 4, 6, false, shrink_xs_kernel<8, 4, 4, 6>, shrink_xs_sk_kernel<8, 4, 4, 6>},       // 23: 128 x 64, 6 steps
-    {4, 24, 4, 3, false, shrink_xs_kernel<4, 24, 4, 3>, shrink_xs_sk_kernel<4, 24, 4, 3>},   // 24: 64 x 384, 3 steps
-    {8, 24, 4, 2, false, shrink_xs_kernel<8, 24, 4, 2>, shrink_xs_sk_kernel<8, 24, 4, 2>},   // 25: 128 x 384, 2 steps
-    {16, 12, 4, 2, false, shrink_xs_kernel<16, 12, 4, 2>, shrink_xs_sk_kernel<16, 12, 4, 2>},   // 26: 256 x 192, 2 steps
 };
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 
