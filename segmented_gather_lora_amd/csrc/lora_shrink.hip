@@ -687,6 +687,8 @@ const StagedCfg kStaged[] = {
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 
 constexpr int kSkMinSteps = 8;   // K steps per workgroup share, at least
+constexpr int kSkBigCfg = 1;     // the 128 x 192 tile
+constexpr long kSkBigShare = 64; // K steps per CU from which it is taken
 
 }  // namespace
 
@@ -773,7 +775,7 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     }
     pl.row_blocks = (rows + rows_per_wg - 1) / rows_per_wg;
 
-    const int tiles_upper = (n + pl.tile_tokens - 1) / pl.tile_tokens + segs;
+    int tiles_upper = (n + pl.tile_tokens - 1) / pl.tile_tokens + segs;
     const int busy = ((n + pl.tile_tokens - 1) / pl.tile_tokens + (segs + 1) / 2) * pl.row_blocks;
     int ks = 1;
     if (!pl.staged && busy < 256) ks = (256 + busy - 1) / busy;
@@ -795,8 +797,25 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     // whose many short, uneven segments leave some CUs with one unit more
     // than others.  LORA_SHRINK_SK=2 forces it for any staged batch that
     // size, LORA_SHRINK_SK=1 turns it off.
-    const bool sk_auto = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0 &&
-                         (ks > 1 || pl.tile_tokens <= 32);
+    const bool automatic = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0;
+    bool sk_auto = automatic && (ks > 1 || pl.tile_tokens <= 32);
+    // Long K walks over more than 128 weight rows (the large shape): the
+    // 128 x 192 tile as stream-K, one workgroup per CU, reads each token row
+    // once per 192 rows instead of once per 128, and its shares are long
+    // enough (at least kSkBigShare steps per CU) to carry the one-deep
+    // occupancy.  On shorter walks (prefill) it loses to the unit tiles.
+    if (automatic && pl.staged && n >= kSkMinTokens && rows > 128) {
+        const StagedCfg &big = kStaged[kSkBigCfg];
+        const long tiles = (n + 16 * big.nt - 1) / (16 * big.nt) + segs;
+        const long rbs = (rows + 16 * big.mr - 1) / (16 * big.mr);
+        if (tiles * rbs * ((hidden + 63) / 64) >= 256L * kSkBigShare) {
+            sk_auto = true;
+            idx = kSkBigCfg;
+            pl.tile_tokens = 16 * big.nt;
+            pl.row_blocks = (int)rbs;
+            tiles_upper = (int)tiles;
+        }
+    }
     if (pl.staged && n >= kSkMinTokens && (cfg.stream_k == 2 || sk_auto)) {
         const StagedCfg &c = kStaged[idx];
         pl.sk = true;

@@ -412,7 +412,7 @@ def test_shrink_staged_full_rows(monkeypatch):
     H.run_and_check(wl, add_inputs=True)
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4, 5, 9, 10, 11, 14, 15])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 9, 10, 11, 14, 15])
 @pytest.mark.parametrize("slices,rank,hidden", [((32,), 32, 1000), ((72, 40, 104), 32, 1000),
                                                 ((64, 64, 64), 64, 520), ((256, 128, 128), 128, 712)])
 @pytest.mark.parametrize("fused", [False, True])
