@@ -185,28 +185,53 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
         }
 
         // D layout: lane holds rows 4g..4g+3 of the m-tile for token column `col`.
+        // With accumulation every old value is loaded before the first store
+        // (a store between them would make each load wait for the previous one).
         if (writer) {
+            float *row_ptr[MT];
+            bool rv[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row0 = rb * rows_per_wg + (wr * MT + mt) * 16 + 4 * g;
-                if (row0 >= a.rows) continue;
-                const int i = row0 / a.rank, j = row0 - i * a.rank;
+                rv[mt] = row0 < a.rows;
+                const int r = rv[mt] ? row0 : 0;
+                const int i = r / a.rank, j = r - i * a.rank;
+                row_ptr[mt] = a.buf + (int64_t)i * a.num_tokens * a.rank + j;
+            }
+            auto dst = [&](int mt, int nt) { return row_ptr[mt] + (int64_t)tok[nt] * a.rank; };
+            if (!atomic && !a.overwrite) {
+                constexpr int G = NT < 2 ? NT : 2;   // n-tiles per round trip
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    if (!tv[nt]) continue;
-                    float *dst = a.buf + ((int64_t)i * a.num_tokens + tok[nt]) * a.rank + j;
-                    const floatx4 v = acc[mt][nt] * a.scale;
-                    if (atomic) {
-                        unsafeAtomicAdd(dst + 0, v[0]);
-                        unsafeAtomicAdd(dst + 1, v[1]);
-                        unsafeAtomicAdd(dst + 2, v[2]);
-                        unsafeAtomicAdd(dst + 3, v[3]);
-                    } else if (a.overwrite) {
-                        *reinterpret_cast<floatx4 *>(dst) = v;
-                    } else {
-                        floatx4 o = *reinterpret_cast<floatx4 *>(dst);
-                        o += v;
-                        *reinterpret_cast<floatx4 *>(dst) = o;
+                for (int n0 = 0; n0 < NT; n0 += G) {
+                    floatx4 old[MT][G];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int q = 0; q < G; ++q)
+                            if (rv[mt] && tv[n0 + q]) old[mt][q] = *reinterpret_cast<const floatx4 *>(dst(mt, n0 + q));
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int q = 0; q < G; ++q)
+                            if (rv[mt] && tv[n0 + q])
+                                *reinterpret_cast<floatx4 *>(dst(mt, n0 + q)) = old[mt][q] + acc[mt][n0 + q] * a.scale;
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        if (!rv[mt] || !tv[nt]) continue;
+                        float *d = dst(mt, nt);
+                        const floatx4 v = acc[mt][nt] * a.scale;
+                        if (atomic) {
+                            unsafeAtomicAdd(d + 0, v[0]);
+                            unsafeAtomicAdd(d + 1, v[1]);
+                            unsafeAtomicAdd(d + 2, v[2]);
+                            unsafeAtomicAdd(d + 3, v[3]);
+                        } else {
+                            *reinterpret_cast<floatx4 *>(d) = v;
+                        }
                     }
                 }
             }
@@ -263,39 +288,75 @@ struct TileLayout {
         floatx4 v[MT][NTW];
     };
 
-    // Writes the piece's sums into buf, scaled.
+    // Writes the piece's sums into buf, scaled.  Every load comes before the
+    // stores it could precede: the tile's token indices first, and with
+    // accumulation the old values of a group of n-tiles before that group's
+    // stores (a store between loads would make each load wait for the one
+    // before it, a memory round trip per 16 x 16 tile).
     __device__ __forceinline__ static void store(const ShrinkArgs &a, const TileRef &tr, int rb,
                                                  const floatx4 (&acc)[MT][NTW], bool atomic) {
         const int lane = lane_id(), wave = wave_id();
         const int wr = wave % WR, wc = wave / WR;
         const int n16 = lane & 15, g = lane >> 4;
         // D layout: lane holds rows 4g..4g+3 of m-tile mt for token column n16 of n-tile nt
+        int tok[NTW];
+        bool tv[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int p = tr.tile * BT + (wc * NTW + nt) * 16 + n16;
-            if (p >= tr.seg_count) continue;
-            int t = a.meta.sorted[tr.seg_start + p];
-            if ((unsigned)t >= (unsigned)a.num_tokens) continue;
+            tok[nt] = a.meta.sorted[tr.seg_start + (p < tr.seg_count ? p : tr.seg_count - 1)];
+            tv[nt] = p < tr.seg_count;
+        }
+        float *row_ptr[MT];
+        bool rv[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int row0 = rb * BR + (wr * MT + mt) * 16 + 4 * g;
-                if (row0 >= a.rows) continue;
-                const int i = row0 / a.rank, jr = row0 - i * a.rank;
-                float *dst = a.buf + ((int64_t)i * a.num_tokens + t) * a.rank + jr;
-                const floatx4 v = acc[mt][nt] * a.scale;
-                if (atomic) {
-                    unsafeAtomicAdd(dst + 0, v[0]);
-                    unsafeAtomicAdd(dst + 1, v[1]);
-                    unsafeAtomicAdd(dst + 2, v[2]);
-                    unsafeAtomicAdd(dst + 3, v[3]);
-                } else if (a.overwrite) {
-                    *reinterpret_cast<floatx4 *>(dst) = v;
-                } else {
-                    floatx4 o = *reinterpret_cast<floatx4 *>(dst);
-                    o += v;
-                    *reinterpret_cast<floatx4 *>(dst) = o;
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row0 = rb * BR + (wr * MT + mt) * 16 + 4 * g;
+            rv[mt] = row0 < a.rows;
+            const int r = rv[mt] ? row0 : 0;
+            const int i = r / a.rank, jr = r - i * a.rank;
+            row_ptr[mt] = a.buf + (int64_t)i * a.num_tokens * a.rank + jr;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) tv[nt] = tv[nt] && (unsigned)tok[nt] < (unsigned)a.num_tokens;
+        auto dst = [&](int mt, int nt) { return row_ptr[mt] + (int64_t)tok[nt] * a.rank; };
+        if (atomic || a.overwrite) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                if (!tv[nt]) continue;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (!rv[mt]) continue;
+                    float *d = dst(mt, nt);
+                    const floatx4 v = acc[mt][nt] * a.scale;
+                    if (atomic) {
+                        unsafeAtomicAdd(d + 0, v[0]);
+                        unsafeAtomicAdd(d + 1, v[1]);
+                        unsafeAtomicAdd(d + 2, v[2]);
+                        unsafeAtomicAdd(d + 3, v[3]);
+                    } else {
+                        *reinterpret_cast<floatx4 *>(d) = v;
+                    }
                 }
             }
+            return;
+        }
+        constexpr int G = NTW < 4 ? NTW : 4;   // n-tiles per round trip
+#pragma unroll
+        for (int n0 = 0; n0 < NTW; n0 += G) {
+            floatx4 old[G][MT];
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (n0 + q < NTW && tv[n0 + q] && rv[mt])
+                        old[q][mt] = *reinterpret_cast<const floatx4 *>(dst(mt, n0 + q));
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (n0 + q < NTW && tv[n0 + q] && rv[mt])
+                        *reinterpret_cast<floatx4 *>(dst(mt, n0 + q)) = old[q][mt] + acc[mt][n0 + q] * a.scale;
         }
     }
 };
