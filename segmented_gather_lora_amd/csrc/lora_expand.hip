@@ -52,6 +52,7 @@ template <int KS, int TT, bool ADD, bool EARLY>
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
     prefetch_kernargs<ExpandArgs>();
     constexpr int kUnitTokens = 16 * TT;
+    constexpr bool kPipe = TT <= 2;             // next block's loads ahead of this block's stores
     constexpr int kRowK = 32 * KS;              // bf16 per staged row (rank padded to 32)
     constexpr int kRowStride = kRowK + 8;       // +16 bytes: rows start on different banks
     extern __shared__ int smem[];
@@ -173,11 +174,12 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
         }
         __syncthreads();
 
+        bool loaded = EARLY;   // this block's operands are in (EARLY, or fetched with the previous block)
         for (int c = 0; c < ncb; ++c) {
             // a wave past the slice's last column stays past it for the rest of the run
             if ((cb0 + c) * kBlockCols + wave * kWaveCols >= width) break;
             const int grp = group_of(c);
-            if (!EARLY || c > 0) load_block(grp);
+            if (!loaded) load_block(grp);
 
             // K positions >= rank: zero the weights (no NaN from stale data)
 #pragma unroll
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
             bias[3] = bf16_bits_to_float(braw[1] >> 16);
             const int ycol = slice_col + grp;
 
+            u32x2 out[kPipe ? TT : 1][4];   // kPipe: the block's results, stored after the next block's loads
 #pragma unroll
             for (int q = 0; q < TT; ++q) {
                 floatx4 acc[4];
@@ -217,10 +220,29 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
                     const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][e] + bias[1]);
                     const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][e] + bias[2]);
                     const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][e] + bias[3]);
-                    __builtin_nontemporal_store(u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
-                                                      pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))},
-                                                reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)));
+                    const u32x2 o = {pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                                     pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
+                    if constexpr (kPipe)
+                        out[q][e] = o;
+                    else
+                        __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)));
                 }
+            }
+            // With tiles of at most 32 tokens, the next block's weights and y
+            // rows go out before this block's stores: memory counters complete
+            // in order, so loads issued after the stores would also wait for
+            // the stores to complete.  (For 64-token tiles the registers this
+            // holds cost more occupancy than the overlap gains.)
+            if constexpr (kPipe) {
+                loaded = c + 1 < ncb && (cb0 + c + 1) * kBlockCols + wave * kWaveCols < width;
+                if (loaded) load_block(group_of(c + 1));
+#pragma unroll
+                for (int q = 0; q < TT; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_nontemporal_store(out[q][e], reinterpret_cast<u32x2 *>(y_at(ytok[q][e], ycol)));
+            } else {
+                loaded = false;
             }
         }
         __syncthreads();   // the staged rows are rewritten by the next piece
