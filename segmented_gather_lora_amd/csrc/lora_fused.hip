@@ -433,46 +433,63 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
         // ---------------- 2. expand blocks idx, idx + W, ... of the tile
         bool waited = false;
         int out = -1;   // thread 0: this workgroup's count-out result
-        for (int blk = idx; blk < f.blocks; blk += W) {
+        // this lane's y rows: tile rows 4g .. 4g + 3, the same for every block
+        int ytok[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            int pp = tr.tile * kTile + 4 * g + r4;
+            pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
+            const int tt = sorted_at(e.meta, smem, tr.seg_start + pp);
+            ytok[r4] = (unsigned)tt < (unsigned)e.num_tokens ? tt : e.num_tokens - 1;
+        }
+        struct Block {
+            int i, width, grp, ycol;
+            bool has_cols;
+            const uint16_t *wslice, *bptr;
+        };
+        auto block_at = [&](int blk) {
+            Block bk;
             int i = 0;
 #pragma unroll
             for (int s = 1; s < LORA_MAX_SLICES; ++s)
                 if (s < e.num_slices && blk >= f.block_begin[s]) i = s;
-            const int width = select_slice(e.width, i);
+            bk.i = i;
+            bk.width = select_slice(e.width, i);
             const int c0 = (blk - select_slice(f.block_begin, i)) * kBlockCols + wave * kWaveCols;
-            const bool has_cols = c0 < width;
-            const int grp = clamp_group((has_cols ? c0 : 0) + 4 * n16, width);
-
-            // weights, bias and y rows first: they do not depend on buf
-            const uint16_t *wslice = select_slice(e.b, i) + (int64_t)tr.lora_id * width * rank;
-            const uint16_t *bptr = select_slice(e.bias, i);
-            const int ycol = select_slice(e.col_off, i) + grp;
-            u32x4 w[4][KS];
-            u32x2 braw, yv[4];
-            int ytok[4];
-            auto load_block = [&]() {
+            bk.has_cols = c0 < bk.width;
+            bk.grp = clamp_group((bk.has_cols ? c0 : 0) + 4 * n16, bk.width);
+            bk.wslice = select_slice(e.b, i) + (int64_t)tr.lora_id * bk.width * rank;
+            bk.bptr = select_slice(e.bias, i);
+            bk.ycol = select_slice(e.col_off, i) + bk.grp;
+            return bk;
+        };
+        // a block's weights, bias and y rows: they do not depend on buf
+        u32x4 w[4][KS];
+        u32x2 braw, yv[4];
+        auto load_block = [&](const Block &bk) {
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const uint16_t *row = wslice + (int64_t)(grp + qq) * rank;
+            for (int qq = 0; qq < 4; ++qq) {
+                const uint16_t *row = bk.wslice + (int64_t)(bk.grp + qq) * rank;
 #pragma unroll
-                    for (int k = 0; k < KS; ++k) {
-                        const int kk = k * 32 + 8 * g;
-                        w[qq][k] = ld16(row + (kk < rank ? kk : 0));
-                    }
+                for (int k = 0; k < KS; ++k) {
+                    const int kk = k * 32 + 8 * g;
+                    w[qq][k] = ld16(row + (kk < rank ? kk : 0));
                 }
-                braw = bptr ? *reinterpret_cast<const u32x2 *>(bptr + (int64_t)tr.lora_id * width + grp) : u32x2{0u, 0u};
+            }
+            braw = bk.bptr ? *reinterpret_cast<const u32x2 *>(bk.bptr + (int64_t)tr.lora_id * bk.width + bk.grp)
+                           : u32x2{0u, 0u};
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    int pp = tr.tile * kTile + 4 * g + r4;
-                    pp = pp < tr.seg_count ? pp : tr.seg_count - 1;
-                    const int tt = sorted_at(e.meta, smem, tr.seg_start + pp);
-                    ytok[r4] = (unsigned)tt < (unsigned)e.num_tokens ? tt : e.num_tokens - 1;
-                    yv[r4] = ADD ? *reinterpret_cast<const u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + ycol)
-                                 : u32x2{0u, 0u};
-                }
-            };
-            load_block();
-
+            for (int r4 = 0; r4 < 4; ++r4)
+                yv[r4] = ADD ? *reinterpret_cast<const u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + bk.ycol)
+                             : u32x2{0u, 0u};
+        };
+        Block cur;
+        if (idx < f.blocks) {
+            cur = block_at(idx);
+            load_block(cur);
+        }
+        for (int blk = idx; blk < f.blocks; blk += W) {
+            const int i = cur.i;
             if (!waited) {   // uniform: the first block of this tile
                 waited = true;
                 // wait for every part; after help_after polls without them,
@@ -545,7 +562,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                 if (tid == 0) out = count_out(words);
             }
 
-            if (has_cols) {
+            u32x2 res[4];
+            if (cur.has_cols) {
                 const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
@@ -580,10 +598,23 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs f) {
                     const float r1 = bf16_bits_to_float(yy[0] >> 16) + (acc[1][r4] + bias[1]);
                     const float r2 = bf16_bits_to_float(yy[1] & 0xffffu) + (acc[2][r4] + bias[2]);
                     const float r3 = bf16_bits_to_float(yy[1] >> 16) + (acc[3][r4] + bias[3]);
-                    *reinterpret_cast<u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + ycol) =
-                        u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
-                              pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
+                    res[r4] = u32x2{pack2(float_to_bf16_bits(r0), float_to_bf16_bits(r1)),
+                                    pack2(float_to_bf16_bits(r2), float_to_bf16_bits(r3))};
                 }
+            }
+            // The next block's operands go out before this block's stores:
+            // memory counters complete in order, so loads issued after the
+            // stores would also wait for the stores to complete.
+            const bool store = cur.has_cols;
+            const int ycol = cur.ycol;
+            if (blk + W < f.blocks) {
+                cur = block_at(blk + W);
+                load_block(cur);
+            }
+            if (store) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<u32x2 *>(e.y + (int64_t)ytok[r4] * e.ldy + ycol) = res[r4];
             }
         }
         // no expand block here: this workgroup is done with its parts, count it out
