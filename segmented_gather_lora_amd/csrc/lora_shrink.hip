@@ -850,27 +850,25 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     pl.k_chunk = chunk;
     pl.units_upper = (long)tiles_upper * pl.row_blocks * ks;
 
-    // Stream-K, with the same tile, for batches of at least kSkMinTokens
-    // tokens (whose library-owned area holds the part slots): where the
-    // model splits K because the units alone would not fill the GPU (the
-    // partial sums are then combined through the slots instead of float
-    // atomics into a cleared buffer), and for tiles of at most 32 tokens,
-    // whose many short, uneven segments leave some CUs with one unit more
-    // than others.  LORA_SHRINK_SK=2 forces it for any staged batch that
-    // size, LORA_SHRINK_SK=1 turns it off.
+    // Stream-K for every staged batch of at least kSkMinTokens tokens (whose
+    // library-owned area holds the part slots): its equal shares leave no CU
+    // with a unit more than another, and a K split needs no float atomics
+    // into a cleared buffer (the slots combine the parts).  The unit walk
+    // stays for smaller batches.  LORA_SHRINK_SK=2 forces it for any staged
+    // batch that size, LORA_SHRINK_SK=1 turns it off.
     const bool automatic = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0;
-    bool sk_auto = automatic && (ks > 1 || pl.tile_tokens <= 32);
+    bool sk_auto = automatic;
     // Long K walks over more than 128 weight rows (the large shape): the
     // 128 x 192 tile as stream-K, one workgroup per CU, reads each token row
     // once per 192 rows instead of once per 128, and its shares are long
     // enough (at least kSkBigShare steps per CU) to carry the one-deep
-    // occupancy.  On shorter walks (prefill) it loses to the unit tiles.
+    // occupancy.  On shorter walks (prefill) it loses to the tile the cost
+    // model picks.
     if (automatic && pl.staged && n >= kSkMinTokens && rows > 128) {
         const StagedCfg &big = kStaged[kSkBigCfg];
         const long tiles = (n + 16 * big.nt - 1) / (16 * big.nt) + segs;
         const long rbs = (rows + 16 * big.mr - 1) / (16 * big.mr);
         if (tiles * rbs * ((hidden + 63) / 64) >= 256L * kSkBigShare) {
-            sk_auto = true;
             idx = kSkBigCfg;
             pl.tile_tokens = 16 * big.nt;
             pl.row_blocks = (int)rbs;
