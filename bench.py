@@ -657,6 +657,12 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
             gr, sr = capture(lambda: [sets[i % rotate].step(path) for i in range(rem)])
             gr.replay()
             PLAN.replay(sr, 1)
+        # the warmup steps once more, from the graph, right before the timed
+        # region: the GPU idles during the captures above, and the first
+        # replays after an idle stretch run slower than the ones after them
+        for _ in range(max(1, math.ceil(warmup / per_graph))):
+            g.replay()
+            PLAN.replay(seq, 1)
         torch.cuda.synchronize()
         PLAN.phase = "timed"
         t0 = time.perf_counter()
