@@ -429,6 +429,18 @@ def test_shrink_stream_k(cfg, slices, rank, hidden, fused, monkeypatch):
     H.run_and_check(wl, add_inputs=True, fused=fused)
 
 
+@pytest.mark.parametrize("n", [1023, 1024, 1100])
+@pytest.mark.parametrize("fused", [False, True])
+def test_shrink_walk_boundary(n, fused):
+    """The automatic choice on both sides of the stream-K threshold (1024
+    tokens: units below, stream-K from there on), with long segments (the
+    LDS-staged kernel), 192 weight rows and K not a multiple of 64."""
+    wl = workloads.random_case(360 + n, n, 1000, (64, 64, 64), 64, 4, bias=True, neg_fraction=0.05)
+    print("shrink walk boundary", n, fused, flush=True)
+    H.run_and_check(wl, add_inputs=True, fused=fused)
+    H.run_and_check(wl, add_inputs=False, fused=fused)
+
+
 @pytest.mark.parametrize("grid", [8, 64, 256])
 def test_shrink_stream_k_many_parts(grid, monkeypatch):
     """Stream-K with more workgroups than the work needs: shares of a step or
