@@ -865,6 +865,65 @@ def test_prepare_fused_graph_replay():
     meta.struct.host_no_lora = None
 
 
+def test_stream_k_graph_replay():
+    """A captured lora_prepare_shrink_expand on a batch the stream-K shrink
+    serves (1500 tokens, long segments), replayed for several batches on
+    fixed buffers (one all -1, one single id, one half -1) with eager work
+    between replays: metadata, buffer and output checked against the oracle
+    after every replay, and the stream-K counters left zero."""
+    sgl = H.lib()
+    base = workloads.random_case(391, 1500, 712, (64, 64, 64), 64, 6, bias=True, neg_fraction=0.05)
+    L = base.layers[0]
+    sp = L.spec
+    n, ml = base.mapping.numel(), base.spec.max_loras
+    meta = sgl.LoraMeta(ml, n)
+    D = H.DevLayer(L)
+    mapping_dev = base.mapping.cuda()
+    buf = torch.zeros((3, n, sp.rank), dtype=torch.float32, device="cuda")
+    y = D.y0.clone()
+
+    def step():
+        sgl.lora_prepare_shrink_expand(mapping_dev, D.x, D.a, D.b, D.bias, buf, y, meta, sp.scale)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(391)
+    y0b = workloads.bf16_bits(L.y0)
+    tokens = np.arange(n, dtype=np.int32)
+    for rep in range(4):
+        m = rng.integers(-1, ml, n).astype(np.int32)
+        if rep == 1:
+            m[:] = -1
+        elif rep == 2:
+            m[:] = 3
+        elif rep == 3:
+            m[rng.random(n) < 0.5] = -1
+        mapping_dev.copy_(torch.from_numpy(m))
+        buf.fill_(-rep - 0.5)   # a fresh buffer per call: its entry contents do not matter
+        y.copy_(D.y0)
+        H.poison_meta(meta)
+        torch.cuda.synchronize()
+        print("stream-K graph replay", rep, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        H.check_meta(meta, m, ml)
+        H.check_sk_clear(meta)
+        buf_ref, y_ref, bound, mag = H.oracle_layer(L, m, ml, tokens, True)
+        buf_g, y_g = buf.cpu().numpy(), H.bits(y)
+        act = m != -1
+        assert np.all(buf_g[:, ~act] == np.float32(-rep - 0.5))
+        if act.any():
+            H.shrink_check(buf_g[:, act], buf_ref[:, act], bound[:, act])
+        H.expand_check(y_g, y_ref, y0b, mag, True, H.propagated(L, m, buf_ref, bound))
+
+
 def _hip_runtime():
     """The HIP runtime library torch has loaded (the same instance, not a second copy)."""
     import ctypes
