@@ -795,7 +795,7 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
 
 
 # LDS-staged shrink configurations the library defines (LORA_SHRINK_STAGED=1..)
-STAGED_CFGS = 24
+STAGED_CFGS = 19
 
 
 def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:

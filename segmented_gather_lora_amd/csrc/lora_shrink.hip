@@ -363,11 +363,8 @@ struct TileLayout {
 
 // The LDS-staged pipeline of one piece of work, shared by the unit-walking
 // and the stream-K kernels: the tile `tr`, the weight rows of row block `rb`,
-// the K range [kbeg, kend).  A step covers KS = 64 or 32 elements of K: the
-// 32-wide step halves a stage, so the same LDS holds twice the stages and
-// keeps more bytes in flight per compute unit (a row's 128-byte line is then
-// requested in two halves, the second from L2).
-template <int NT, int MR, int WR, int STAGES, int KS = 64>
+// the K range [kbeg, kend).
+template <int NT, int MR, int WR, int STAGES>
 struct Staged : TileLayout<NT, MR, WR> {
     using L = TileLayout<NT, MR, WR>;
     using typename L::Acc;
@@ -376,26 +373,12 @@ struct Staged : TileLayout<NT, MR, WR> {
     using L::MT;
     using L::NTW;
     static constexpr int NSTAGE = STAGES;
-    static constexpr int KSTEP = KS;
-    static constexpr int CH = KS / 8;             // 16-byte chunks of a row per step
-    static constexpr int ROW_BYTES = 2 * KS;      // bytes of a row per step
-    static constexpr int RPI = 64 / CH;           // rows per load instruction (1 KB)
-    static constexpr int HALVES = KS / 32;        // 32-wide MFMA steps per step
     static constexpr int ROWS = BT + BR;
-    static constexpr int INSTR = ROWS / (4 * RPI);   // load instructions per wave per step
-    static constexpr bool SPLIT_H = HALVES == 2 && MT * NTW >= 40;
-    static constexpr int NQ = HALVES == 2 && !SPLIT_H ? 2 : 1;   // halves read before the first MFMA
-    static_assert(KS == 64 || KS == 32, "K step");
-    static_assert(ROWS % (4 * RPI) == 0, "tile shape");
+    static constexpr int INSTR = ROWS / 32;     // load instructions per wave per step
+    static constexpr bool SPLIT_H = MT * NTW >= 40;
+    static_assert(ROWS % 32 == 0, "tile shape");
     static_assert((STAGES - 1) * INSTR < 64, "vmcnt range");
-    typedef unsigned char Stage[ROWS * ROW_BYTES];
-
-    // LDS slot of chunk c of tile row r.  The MFMA operand reads take one
-    // chunk from each of 8 (or 16) consecutive rows; the XOR spreads them
-    // over distinct 16-byte bank groups of a 128-byte (256-byte) window.
-    __device__ __forceinline__ static int slot(int r, int c) {
-        return KS == 64 ? (c ^ (r & 7)) : (c ^ (((r >> 1) ^ (r >> 3)) & 3));
-    }
+    typedef unsigned char Stage[ROWS * 128];
 
     // (The sums are returned by value: the loop then works on values of its
     // own, which keeps the accumulators in place across iterations.)
@@ -406,17 +389,17 @@ struct Staged : TileLayout<NT, MR, WR> {
         const int lane = lane_id(), wave = wave_id();
         const int wr = wave % WR, wc = wave / WR;
         const int n16 = lane & 15, g = lane >> 4;
-        const int nsteps = (kend - kbeg + KS - 1) / KS;
+        const int nsteps = (kend - kbeg + 63) / 64;
 
-        // this lane's source rows: instruction j covers tile rows
-        // (wave*INSTR + j)*RPI .. +RPI; the lane lands in slot lane % CH of
-        // row lane / CH, so it loads the chunk that slot() puts there
+        // this lane's source rows: instruction j covers tile rows (wave*INSTR + j)*8 .. +8
+        // every instruction's 8 rows start at a multiple of 8, so the lane's
+        // row index mod 8 and with it its global chunk (landing in slot
+        // lane & 7) are the same for all of them
+        const int chunk_k = 8 * ((lane & 7) ^ ((lane >> 3) & 7));
         const uint16_t *src[INSTR];
-        int chunk_k[INSTR];
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
-            const int r = (wave * INSTR + j) * RPI + lane / CH;
-            chunk_k[j] = 8 * slot(r, lane % CH);
+            const int r = (wave * INSTR + j) * 8 + (lane >> 3);
             if (r < BT) {
                 int p = tr.tile * BT + r;
                 p = p < tr.seg_count ? p : tr.seg_count - 1;
@@ -434,7 +417,7 @@ struct Staged : TileLayout<NT, MR, WR> {
             const int sc = step < nsteps ? step : nsteps - 1;   // past the end: reload, never skip
 #pragma unroll
             for (int j = 0; j < INSTR; ++j) {
-                const int k = kbeg + sc * KS + chunk_k[j];
+                const int k = kbeg + sc * 64 + chunk_k;
                 const uint16_t *gp = src[j] + (k + 8 <= kend ? k : 0);
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gp),
                                                  reinterpret_cast<void *>(&stage[buf][(wave * INSTR + j) * 1024]),
@@ -457,23 +440,22 @@ struct Staged : TileLayout<NT, MR, WR> {
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("" ::: "memory");
             const unsigned char *sb = stage[s % STAGES];
-            const bool mask = s == nsteps - 1 && ((kend - kbeg) % KS) != 0;
-            // the operands of every 32-wide half of the step, read before the
+            const bool mask = s == nsteps - 1 && ((kend - kbeg) & 63) != 0;
+            // the operands of both 32-wide halves of the step, read before the
             // first MFMA; with SPLIT_H (tiles whose accumulators leave no room
-            // for both) each half is read just before its MFMAs.  Lane group
-            // g takes chunk 2g + h of the 64-wide step (g of the 32-wide one).
-            u32x4 xa[NQ][NTW], wa[NQ][MT];
+            // for both) each half is read just before its MFMAs
+            u32x4 xa[SPLIT_H ? 1 : 2][NTW], wa[SPLIT_H ? 1 : 2][MT];
             auto read_half = [&](int h, int q) {
-                const int c = HALVES * g + h;
+                const int c = 2 * g + h;
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const int r = (wc * NTW + nt) * 16 + n16;
-                    xa[q][nt] = lds_read16(sb + r * ROW_BYTES + 16 * slot(r, c));
+                    xa[q][nt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const int r = BT + (wr * MT + mt) * 16 + n16;
-                    wa[q][mt] = lds_read16(sb + r * ROW_BYTES + 16 * slot(r, c));
+                    wa[q][mt] = lds_read16(sb + r * 128 + 16 * (c ^ (r & 7)));
                 }
             };
             auto wait_half = [&](int q) {
@@ -483,21 +465,21 @@ struct Staged : TileLayout<NT, MR, WR> {
                 for (int mt = 0; mt < MT; ++mt) after_wait(wa[q][mt]);
             };
             if (!SPLIT_H) {
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) read_half(q, q);
+                read_half(0, 0);
+                read_half(1, SPLIT_H ? 0 : 1);
                 lds_wait();
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) wait_half(q);
+                wait_half(0);
+                wait_half(SPLIT_H ? 0 : 1);
             }
 #pragma unroll
-            for (int h = 0; h < HALVES; ++h) {
+            for (int h = 0; h < 2; ++h) {
                 const int q = SPLIT_H ? 0 : h;
                 if (SPLIT_H) {
                     read_half(h, 0);
                     lds_wait();
                     wait_half(0);
                 }
-                if (mask && kbeg + s * KS + 8 * (HALVES * g + h) + 8 > kend) {
+                if (mask && kbeg + s * 64 + 8 * (2 * g + h) + 8 > kend) {
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) xa[q][nt] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -541,9 +523,9 @@ __device__ __forceinline__ void unit_walk(const ShrinkArgs &a, int *smem, int *s
     }
 }
 
-template <int NT, int MR, int WR, int STAGES, int KS = 64>
+template <int NT, int MR, int WR, int STAGES>
 __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
-    using S = Staged<NT, MR, WR, STAGES, KS>;
+    using S = Staged<NT, MR, WR, STAGES>;
     extern __shared__ int smem[];
     __shared__ int s_wsum[kThreads / kWave];
     __shared__ __attribute__((aligned(1024))) typename S::Stage stage[STAGES];
@@ -551,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void shrink_lds_kernel(ShrinkArgs a) {
 }
 
 // Stream-K form of the LDS-staged shrink.  The work is the list of (tile,
-// K step) pairs, tile-major.  Workgroups form groups of RB, one per
+// 64-wide K step) pairs, tile-major.  Workgroups form groups of RB, one per
 // row block of the layer's weight rows; the groups (G of them, about two
 // workgroups per CU in all) take equal contiguous shares of the list, the
 // shares in XCD order (workgroup b sits on XCD b % 8, so consecutive shares
@@ -586,7 +568,7 @@ __device__ __forceinline__ void sk_walk(const ShrinkArgs &a, const SkArgs &sk, i
     const int total = build_tile_table<kThreads>(a.meta, S::BT, smem, s_wsum);
     const int tid = threadIdx.x;
     const int RB = a.row_blocks;
-    const int nsteps = (a.hidden + S::KSTEP - 1) / S::KSTEP;
+    const int nsteps = (a.hidden + 63) / 64;
     const long W = (long)total * nsteps;
     // groups per XCD (the launcher makes it at least one); with fewer steps
     // than groups only the first W groups are used, so that every share in
@@ -611,7 +593,7 @@ __device__ __forceinline__ void sk_walk(const ShrinkArgs &a, const SkArgs &sk, i
         const int s1 = (int)min((long)nsteps, (long)s0 + (end - cur));
         cur += s1 - s0;
         const TileRef tr = lookup_tile(smem, nslots, t);
-        typename S::Acc res = S::run(a, tr, r, S::KSTEP * s0, min(S::KSTEP * s1, a.hidden), stage);
+        typename S::Acc res = S::run(a, tr, r, 64 * s0, min(64 * s1, a.hidden), stage);
         floatx4 (&acc)[S::MT][S::NTW] = res.v;
         if (s0 > 0 || s1 < nsteps) {
             const long first = (long)t * nsteps;
@@ -666,9 +648,9 @@ __device__ __forceinline__ void sk_walk(const ShrinkArgs &a, const SkArgs &sk, i
     }
 }
 
-template <int NT, int MR, int WR, int STAGES, int KS = 64>
+template <int NT, int MR, int WR, int STAGES>
 __global__ __launch_bounds__(kThreads) void shrink_sk_kernel(ShrinkArgs a, SkArgs sk) {
-    using S = Staged<NT, MR, WR, STAGES, KS>;
+    using S = Staged<NT, MR, WR, STAGES>;
     extern __shared__ int smem[];
     __shared__ int s_wsum[kThreads / kWave];
     __shared__ __attribute__((aligned(1024))) typename S::Stage stage[STAGES];
@@ -734,41 +716,34 @@ ShrinkFn pick(int nt, int wk, int mt) {
 }
 
 
-// LDS-staged configurations: tokens x rows per workgroup, wave layout, stages,
-// K step.
+// LDS-staged configurations: tokens x rows per workgroup, wave layout, stages.
 typedef void (*SkFn)(ShrinkArgs, SkArgs);
 struct StagedCfg {
-    int nt, mr, wr, stages, ks;
+    int nt, mr, wr, stages;
     bool automatic;   // eligible for the automatic choice
     ShrinkFn fn;
     SkFn sk;          // the same tile in the stream-K kernel
 };
 const StagedCfg kStaged[] = {
-    {4, 12, 4, 3, 64, true, shrink_lds_kernel<4, 12, 4, 3>, shrink_sk_kernel<4, 12, 4, 3>},    // 0: 64 tokens x 192 rows
-    {8, 12, 4, 3, 64, false, shrink_lds_kernel<8, 12, 4, 3>, shrink_sk_kernel<8, 12, 4, 3>},   // 1: 128 x 192 (one wave per SIMD: slow)
-    {4, 8, 4, 4, 64, true, shrink_lds_kernel<4, 8, 4, 4>, shrink_sk_kernel<4, 8, 4, 4>},      // 2: 64 x 128
-    {4, 4, 4, 4, 64, true, shrink_lds_kernel<4, 4, 4, 4>, shrink_sk_kernel<4, 4, 4, 4>},      // 3: 64 x 64
-    {4, 2, 2, 4, 64, true, shrink_lds_kernel<4, 2, 2, 4>, shrink_sk_kernel<4, 2, 2, 4>},      // 4: 64 x 32
-    {2, 12, 4, 4, 64, true, shrink_lds_kernel<2, 12, 4, 4>, shrink_sk_kernel<2, 12, 4, 4>},    // 5: 32 x 192
-    {8, 4, 4, 4, 64, true, shrink_lds_kernel<8, 4, 4, 4>, shrink_sk_kernel<8, 4, 4, 4>},      // 6: 128 x 64
-    {8, 2, 2, 4, 64, true, shrink_lds_kernel<8, 2, 2, 4>, shrink_sk_kernel<8, 2, 2, 4>},      // 7: 128 x 32
-    {2, 4, 4, 4, 64, true, shrink_lds_kernel<2, 4, 4, 4>, shrink_sk_kernel<2, 4, 4, 4>},      // 8: 32 x 64
-    {2, 2, 2, 4, 64, true, shrink_lds_kernel<2, 2, 2, 4>, shrink_sk_kernel<2, 2, 2, 4>},      // 9: 32 x 32
-    {4, 6, 2, 5, 64, true, shrink_lds_kernel<4, 6, 2, 5>, shrink_sk_kernel<4, 6, 2, 5>},      // 10: 64 x 96
-    {8, 6, 2, 4, 64, true, shrink_lds_kernel<8, 6, 2, 4>, shrink_sk_kernel<8, 6, 2, 4>},      // 11: 128 x 96
-    {8, 8, 4, 4, 64, false, shrink_lds_kernel<8, 8, 4, 4>, shrink_sk_kernel<8, 8, 4, 4>},     // 12: 128 x 128, 4 stages (one per CU)
-    {8, 8, 4, 2, 64, true, shrink_lds_kernel<8, 8, 4, 2>, shrink_sk_kernel<8, 8, 4, 2>},      // 13: 128 x 128, 2 stages (two per CU)
-    {4, 6, 2, 3, 64, false, shrink_lds_kernel<4, 6, 2, 3>, shrink_sk_kernel<4, 6, 2, 3>},     // 14: 64 x 96, 3 stages (two per CU)
-    {4, 6, 2, 7, 64, false, shrink_lds_kernel<4, 6, 2, 7>, shrink_sk_kernel<4, 6, 2, 7>},     // 15: 64 x 96, 7 stages
-    {2, 4, 4, 10, 64, false, shrink_lds_kernel<2, 4, 4, 10>, shrink_sk_kernel<2, 4, 4, 10>},   // 16: 32 x 64, 10 stages
-    {4, 4, 4, 8, 64, false, shrink_lds_kernel<4, 4, 4, 8>, shrink_sk_kernel<4, 4, 4, 8>},     // 17: 64 x 64, 8 stages
-    {2, 2, 2, 12, 64, false, shrink_lds_kernel<2, 2, 2, 12>, shrink_sk_kernel<2, 2, 2, 12>},   // 18: 32 x 32, 12 stages
-    // 32-wide K steps: half-size stages, twice as many in the same LDS
-    {8, 12, 4, 7, 32, false, shrink_lds_kernel<8, 12, 4, 7, 32>, shrink_sk_kernel<8, 12, 4, 7, 32>},  // 19: 128 x 192
-    {4, 12, 4, 8, 32, false, shrink_lds_kernel<4, 12, 4, 8, 32>, shrink_sk_kernel<4, 12, 4, 8, 32>},  // 20: 64 x 192
-    {8, 8, 4, 8, 32, false, shrink_lds_kernel<8, 8, 4, 8, 32>, shrink_sk_kernel<8, 8, 4, 8, 32>},     // 21: 128 x 128
-    {4, 4, 4, 8, 32, false, shrink_lds_kernel<4, 4, 4, 8, 32>, shrink_sk_kernel<4, 4, 4, 8, 32>},     // 22: 64 x 64
-    {2, 6, 2, 8, 32, false, shrink_lds_kernel<2, 6, 2, 8, 32>, shrink_sk_kernel<2, 6, 2, 8, 32>},     // 23: 32 x 96
+    {4, 12, 4, 3, true, shrink_lds_kernel<4, 12, 4, 3>, shrink_sk_kernel<4, 12, 4, 3>},    // 0: 64 tokens x 192 rows
+    {8, 12, 4, 3, false, shrink_lds_kernel<8, 12, 4, 3>, shrink_sk_kernel<8, 12, 4, 3>},   // 1: 128 x 192 (one wave per SIMD: slow)
+    {4, 8, 4, 4, true, shrink_lds_kernel<4, 8, 4, 4>, shrink_sk_kernel<4, 8, 4, 4>},      // 2: 64 x 128
+    {4, 4, 4, 4, true, shrink_lds_kernel<4, 4, 4, 4>, shrink_sk_kernel<4, 4, 4, 4>},      // 3: 64 x 64
+    {4, 2, 2, 4, true, shrink_lds_kernel<4, 2, 2, 4>, shrink_sk_kernel<4, 2, 2, 4>},      // 4: 64 x 32
+    {2, 12, 4, 4, true, shrink_lds_kernel<2, 12, 4, 4>, shrink_sk_kernel<2, 12, 4, 4>},    // 5: 32 x 192
+    {8, 4, 4, 4, true, shrink_lds_kernel<8, 4, 4, 4>, shrink_sk_kernel<8, 4, 4, 4>},      // 6: 128 x 64
+    {8, 2, 2, 4, true, shrink_lds_kernel<8, 2, 2, 4>, shrink_sk_kernel<8, 2, 2, 4>},      // 7: 128 x 32
+    {2, 4, 4, 4, true, shrink_lds_kernel<2, 4, 4, 4>, shrink_sk_kernel<2, 4, 4, 4>},      // 8: 32 x 64
+    {2, 2, 2, 4, true, shrink_lds_kernel<2, 2, 2, 4>, shrink_sk_kernel<2, 2, 2, 4>},      // 9: 32 x 32
+    {4, 6, 2, 5, true, shrink_lds_kernel<4, 6, 2, 5>, shrink_sk_kernel<4, 6, 2, 5>},      // 10: 64 x 96
+    {8, 6, 2, 4, true, shrink_lds_kernel<8, 6, 2, 4>, shrink_sk_kernel<8, 6, 2, 4>},      // 11: 128 x 96
+    {8, 8, 4, 4, false, shrink_lds_kernel<8, 8, 4, 4>, shrink_sk_kernel<8, 8, 4, 4>},     // 12: 128 x 128, 4 stages (one per CU)
+    {8, 8, 4, 2, true, shrink_lds_kernel<8, 8, 4, 2>, shrink_sk_kernel<8, 8, 4, 2>},      // 13: 128 x 128, 2 stages (two per CU)
+    {4, 6, 2, 3, false, shrink_lds_kernel<4, 6, 2, 3>, shrink_sk_kernel<4, 6, 2, 3>},     // 14: 64 x 96, 3 stages (two per CU)
+    {4, 6, 2, 7, false, shrink_lds_kernel<4, 6, 2, 7>, shrink_sk_kernel<4, 6, 2, 7>},     // 15: 64 x 96, 7 stages
+    {2, 4, 4, 10, false, shrink_lds_kernel<2, 4, 4, 10>, shrink_sk_kernel<2, 4, 4, 10>},   // 16: 32 x 64, 10 stages
+    {4, 4, 4, 8, false, shrink_lds_kernel<4, 4, 4, 8>, shrink_sk_kernel<4, 4, 4, 8>},     // 17: 64 x 64, 8 stages
+    {2, 2, 2, 12, false, shrink_lds_kernel<2, 2, 2, 12>, shrink_sk_kernel<2, 2, 2, 12>},   // 18: 32 x 32, 12 stages
 };
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 
@@ -908,7 +883,7 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
         pl.slot_floats = 256 * c.nt * c.mr;
         pl.k_splits = 1;
         pl.k_chunk = (hidden + 63) / 64 * 64;
-        // 64-wide K steps of the list, at most (the share sizes count in these)
+        // K steps of the list, at most
         pl.units_upper = (long)tiles_upper * ((hidden + 63) / 64);
     }
     return pl;

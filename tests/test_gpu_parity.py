@@ -392,12 +392,11 @@ def test_invalid_arguments_raise():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg", [*range(1, 16), *range(20, 25)])
+@pytest.mark.parametrize("cfg", range(1, 16))
 @pytest.mark.parametrize("ks", [1, 3])
 def test_shrink_staged_variants(cfg, ks, monkeypatch):
-    """LDS-staged shrink configurations (64- and 32-wide K steps) on a ragged
-    case: K not a multiple of 64 (nor of 32), rows not a multiple of the row
-    block, short segments."""
+    """Every LDS-staged shrink configuration on a ragged case: K not a
+    multiple of 64, rows not a multiple of the row block, short segments."""
     monkeypatch.setenv("LORA_SHRINK_VARIANT", "3")
     monkeypatch.setenv("LORA_SHRINK_STAGED", str(cfg))
     monkeypatch.setenv("LORA_SHRINK_KSPLIT", str(ks))
@@ -413,7 +412,7 @@ def test_shrink_staged_full_rows(monkeypatch):
     H.run_and_check(wl, add_inputs=True)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 9, 10, 11, 14, 15, 20, 21, 22, 23, 24])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 9, 10, 11, 14, 15])
 @pytest.mark.parametrize("slices,rank,hidden", [((32,), 32, 1000), ((72, 40, 104), 32, 1000),
                                                 ((64, 64, 64), 64, 520), ((256, 128, 128), 128, 712)])
 @pytest.mark.parametrize("fused", [False, True])
