@@ -250,11 +250,14 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a) {
 // element is fetched once per workgroup.  The 16-byte chunks of row r are
 // stored XOR-swizzled (chunk c at slot c ^ (r & 7)) so that the MFMA operand
 // reads (ds_read_b128 of one chunk from 8 different rows) hit 8 different
-// bank groups.  STAGES steps are in flight; a wave waits only for the step it
-// is about to use (s_waitcnt vmcnt), then a barrier publishes the step to the
-// whole workgroup.  Waves split the tile as WR row groups x (4 / WR) token
-// groups; each output element belongs to one wave, so K chunks are combined
-// only across workgroups (float atomics), never inside one.
+// bank groups.  All STAGES stages are filled ahead; a wave waits only for the
+// step it is about to use (s_waitcnt vmcnt), then a barrier publishes the step
+// to the whole workgroup.  Once every wave has read its MFMA operands of the
+// step into registers, a second barrier frees the stage and the step STAGES
+// ahead is issued into it before the MFMAs run, so that STAGES steps stay in
+// flight behind the arithmetic.  Waves split the tile as WR row groups x
+// (4 / WR) token groups; each output element belongs to one wave, so K
+// chunks are combined only across workgroups, never inside one.
 __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
     return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
@@ -341,7 +344,9 @@ struct TileLayout {
             }
             return;
         }
-        constexpr int G = NTW < 4 ? NTW : 4;   // n-tiles per round trip
+        // n-tiles per round trip: all of them when their old values fit in 24
+        // 16-byte registers, else 4
+        constexpr int G = MT * NTW <= 24 ? NTW : (NTW < 4 ? NTW : 4);
 #pragma unroll
         for (int n0 = 0; n0 < NTW; n0 += G) {
             floatx4 old[G][MT];
@@ -375,66 +380,104 @@ struct Staged : TileLayout<NT, MR, WR> {
     static constexpr int NSTAGE = STAGES;
     static constexpr int ROWS = BT + BR;
     static constexpr int INSTR = ROWS / 32;     // load instructions per wave per step
-    static constexpr bool SPLIT_H = MT * NTW >= 40;
     static_assert(ROWS % 32 == 0, "tile shape");
-    static_assert((STAGES - 1) * INSTR < 64, "vmcnt range");
+    static_assert(STAGES * INSTR < 64, "vmcnt range");
     typedef unsigned char Stage[ROWS * 128];
 
-    // (The sums are returned by value: the loop then works on values of its
-    // own, which keeps the accumulators in place across iterations.)
-    __device__ __forceinline__ static Acc run(const ShrinkArgs &a, const TileRef &tr, int rb, int kbeg, int kend,
-                                              Stage *stage) {
-        Acc out;
-        floatx4 (&acc)[MT][NTW] = out.v;
-        const int lane = lane_id(), wave = wave_id();
-        const int wr = wave % WR, wc = wave / WR;
-        const int n16 = lane & 15, g = lane >> 4;
-        const int nsteps = (kend - kbeg + 63) / 64;
+    // A piece's source rows and K range.  The runner has three phases:
+    //   sources  loads the sorted indices of the piece's token rows;
+    //   prime    turns them into row pointers and issues the first STAGES
+    //            steps;
+    //   finish   runs every step and drains the pipeline.
+    struct Src {
+        const uint16_t *w[INSTR];   // weight rows (instructions over token rows: unused)
+        int tok[INSTR];             // token rows: the sorted index
+        int kbeg, kend, nsteps;
+    };
 
-        // this lane's source rows: instruction j covers tile rows (wave*INSTR + j)*8 .. +8
-        // every instruction's 8 rows start at a multiple of 8, so the lane's
-        // row index mod 8 and with it its global chunk (landing in slot
-        // lane & 7) are the same for all of them
-        const int chunk_k = 8 * ((lane & 7) ^ ((lane >> 3) & 7));
-        const uint16_t *src[INSTR];
+    // this lane's source rows: instruction j covers tile rows (wave*INSTR + j)*8 .. +8
+    // (every instruction's 8 rows lie on one side of BT, a multiple of 16)
+    __device__ __forceinline__ static Src sources(const ShrinkArgs &a, const TileRef &tr, int rb, int kbeg,
+                                                  int kend) {
+        Src sr;
+        const int lane = lane_id(), wave = wave_id();
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
             const int r = (wave * INSTR + j) * 8 + (lane >> 3);
             if (r < BT) {
                 int p = tr.tile * BT + r;
                 p = p < tr.seg_count ? p : tr.seg_count - 1;
-                int t = a.meta.sorted[tr.seg_start + p];
-                t = (unsigned)t < (unsigned)a.num_tokens ? t : 0;
-                src[j] = a.x + (int64_t)t * a.ldx;
+                sr.tok[j] = a.meta.sorted[tr.seg_start + p];
+                sr.w[j] = a.x;
             } else {
                 int row = rb * BR + (r - BT);
                 row = row < a.rows ? row : a.rows - 1;
                 const int i = row / a.rank, jr = row - i * a.rank;
-                src[j] = select_slice(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
+                sr.tok[j] = 0;
+                sr.w[j] = select_slice(a.a, i) + ((int64_t)tr.lora_id * a.rank + jr) * a.hidden;
             }
         }
-        auto issue = [&](int step, int buf) {
-            const int sc = step < nsteps ? step : nsteps - 1;   // past the end: reload, never skip
+        sr.kbeg = kbeg;
+        sr.kend = kend;
+        sr.nsteps = (kend - kbeg + 63) / 64;
+        return sr;
+    }
+
+    // every instruction's 8 rows start at a multiple of 8, so the lane's row
+    // index mod 8 and with it its global chunk (landing in slot lane & 7)
+    // are the same for all of them
+    __device__ __forceinline__ static int chunk_k() {
+        const int lane = lane_id();
+        return 8 * ((lane & 7) ^ ((lane >> 3) & 7));
+    }
+
+    __device__ __forceinline__ static void issue(const Src &sr, const uint16_t *const (&src)[INSTR], int step,
+                                                 int buf, Stage *stage) {
+        const int wave = wave_id();
+        const int sc = step < sr.nsteps ? step : sr.nsteps - 1;   // past the end: reload, never skip
+        const int k = sr.kbeg + sc * 64 + chunk_k();
+        const int off = k + 8 <= sr.kend ? k : 0;
 #pragma unroll
-            for (int j = 0; j < INSTR; ++j) {
-                const int k = kbeg + sc * 64 + chunk_k;
-                const uint16_t *gp = src[j] + (k + 8 <= kend ? k : 0);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gp),
-                                                 reinterpret_cast<void *>(&stage[buf][(wave * INSTR + j) * 1024]),
-                                                 16, 0, 0);
-            }
-        };
+        for (int j = 0; j < INSTR; ++j)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src[j] + off),
+                                             reinterpret_cast<void *>(&stage[buf][(wave * INSTR + j) * 1024]), 16,
+                                             0, 0);
+    }
+
+    // The row pointers (the first use of the sorted indices, whose loads are
+    // waited for here), then the first STAGES steps.
+    __device__ __forceinline__ static void prime(const ShrinkArgs &a, Src &sr, const uint16_t *(&src)[INSTR],
+                                                 Stage *stage) {
+        const int lane = lane_id(), wave = wave_id();
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            asm volatile("" : "+v"(sr.tok[j]));
+            const int r = (wave * INSTR + j) * 8 + (lane >> 3);
+            const int t = (unsigned)sr.tok[j] < (unsigned)a.num_tokens ? sr.tok[j] : 0;
+            src[j] = r < BT ? a.x + (int64_t)t * a.ldx : sr.w[j];
+        }
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) issue(sr, src, st, st, stage);
+    }
+
+    // (The sums are returned by value: the loop then works on values of its
+    // own, which keeps the accumulators in place across iterations.)
+    __device__ __forceinline__ static Acc finish(const Src &sr, const uint16_t *const (&src)[INSTR], Stage *stage) {
+        Acc out;
+        floatx4 (&acc)[MT][NTW] = out.v;
+        const int lane = lane_id(), wave = wave_id();
+        const int wr = wave % WR, wc = wave / WR;
+        const int n16 = lane & 15, g = lane >> 4;
+        const int kbeg = sr.kbeg, kend = sr.kend, nsteps = sr.nsteps;
 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st) issue(st, st);
-
         for (int s = 0; s < nsteps; ++s) {
-            issue(s + STAGES - 1, (s + STAGES - 1) % STAGES);
+            // step s has landed once only the STAGES - 1 steps after it are
+            // outstanding; the barrier publishes it to every wave
             __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 1) * INSTR));
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
@@ -442,9 +485,8 @@ struct Staged : TileLayout<NT, MR, WR> {
             const unsigned char *sb = stage[s % STAGES];
             const bool mask = s == nsteps - 1 && ((kend - kbeg) & 63) != 0;
             // the operands of both 32-wide halves of the step, read before the
-            // first MFMA; with SPLIT_H (tiles whose accumulators leave no room
-            // for both) each half is read just before its MFMAs
-            u32x4 xa[SPLIT_H ? 1 : 2][NTW], wa[SPLIT_H ? 1 : 2][MT];
+            // first MFMA
+            u32x4 xa[2][NTW], wa[2][MT];
             auto read_half = [&](int h, int q) {
                 const int c = 2 * g + h;
 #pragma unroll
@@ -464,21 +506,20 @@ struct Staged : TileLayout<NT, MR, WR> {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) after_wait(wa[q][mt]);
             };
-            if (!SPLIT_H) {
-                read_half(0, 0);
-                read_half(1, SPLIT_H ? 0 : 1);
-                lds_wait();
-                wait_half(0);
-                wait_half(SPLIT_H ? 0 : 1);
-            }
+            read_half(0, 0);
+            read_half(1, 1);
+            lds_wait();
+            wait_half(0);
+            wait_half(1);
+            // every wave has read the stage: refill it with step s + STAGES
+            // before the MFMAs, so that STAGES steps are in flight while
+            // they run
+            __builtin_amdgcn_s_barrier();
+            issue(sr, src, s + STAGES, s % STAGES, stage);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int q = SPLIT_H ? 0 : h;
-                if (SPLIT_H) {
-                    read_half(h, 0);
-                    lds_wait();
-                    wait_half(0);
-                }
+                const int q = h;
                 if (mask && kbeg + s * 64 + 8 * (2 * g + h) + 8 > kend) {
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) xa[q][nt] = u32x4{0u, 0u, 0u, 0u};
@@ -491,12 +532,21 @@ struct Staged : TileLayout<NT, MR, WR> {
                     for (int nt = 0; nt < NTW; ++nt)
                         acc[mt][nt] = mfma16x16x32(as_bf16x8(wa[q][mt]), as_bf16x8(xa[q][nt]), acc[mt][nt]);
             }
-            __builtin_amdgcn_s_barrier();   // every wave has read the stage: it may be refilled
         }
         // drain the dummy loads issued past the end before the stages are reused
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();
         return out;
+    }
+
+    // One piece start to end: the tile `tr`, the weight rows of row block
+    // `rb`, the K range [kbeg, kend).
+    __device__ __forceinline__ static Acc run(const ShrinkArgs &a, const TileRef &tr, int rb, int kbeg, int kend,
+                                              Stage *stage) {
+        Src sr = sources(a, tr, rb, kbeg, kend);
+        const uint16_t *src[INSTR];
+        prime(a, sr, src, stage);
+        return finish(sr, src, stage);
     }
 };
 
@@ -627,7 +677,7 @@ __device__ __forceinline__ void sk_walk(const ShrinkArgs &a, const SkArgs &sk, i
             __syncthreads();
             // the later parts' sums, up to 16 16-byte loads in flight at a time
             constexpr int P = S::MT * S::NTW;
-            constexpr int B = P < 16 ? P : 16;
+            constexpr int B = P < 24 ? P : 24;
             for (int k = gq + 1; k <= gb; ++k) {
                 const __amdgpu_buffer_rsrc_t slot = slot_rsrc(k);
 #pragma unroll
@@ -747,6 +797,7 @@ const StagedCfg kStaged[] = {
 };
 constexpr int kNumStaged = sizeof(kStaged) / sizeof(kStaged[0]);
 
+constexpr int kStagedGridCap = 512;   // workgroups of the staged unit walk, at most
 constexpr int kSkMinSteps = 8;   // K steps per workgroup share, at least
 constexpr int kSkBigCfg = 1;     // the 128 x 192 tile
 constexpr long kSkBigShare = 64; // K steps per CU from which it is taken
@@ -850,14 +901,22 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     pl.k_chunk = chunk;
     pl.units_upper = (long)tiles_upper * pl.row_blocks * ks;
 
-    // Stream-K for every staged batch of at least kSkMinTokens tokens (whose
+    // Stream-K for staged batches of at least kSkMinTokens tokens (whose
     // library-owned area holds the part slots): its equal shares leave no CU
     // with a unit more than another, and a K split needs no float atomics
     // into a cleared buffer (the slots combine the parts).  The unit walk
-    // stays for smaller batches.  LORA_SHRINK_SK=2 forces it for any staged
-    // batch that size, LORA_SHRINK_SK=1 turns it off.
+    // stays for smaller batches, and for batches whose units need no K split
+    // and all fit on the GPU at once (at most one unit per workgroup of the
+    // unit walk's grid): each workgroup then runs one whole unit, as even as
+    // the shares and with no parts to combine.  LORA_SHRINK_SK=2 forces
+    // stream-K for any staged batch that size, LORA_SHRINK_SK=1 turns it off.
     const bool automatic = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0;
     bool sk_auto = automatic;
+    if (automatic && pl.staged && pl.k_splits == 1) {
+        const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1);
+        const long slots = resident_grid(reinterpret_cast<const void *>(pl.fn), kThreads, lds);
+        if (pl.units_upper <= (slots < kStagedGridCap ? slots : kStagedGridCap)) sk_auto = false;
+    }
     // Long K walks over more than 128 weight rows (the large shape): the
     // 128 x 192 tile as stream-K, one workgroup per CU, reads each token row
     // once per 192 rows instead of once per 128, and its shares are long
@@ -959,7 +1018,7 @@ hipError_t launch_shrink(const ShrinkArgs &in, const SkArgs &sk, const ShrinkTun
     // small batches: the direct-load kernel keeps the sorted indices in LDS
     a.meta.lds_tokens = (!pl.staged && n <= kLdsTokensMax) ? n : 0;
     const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1 + a.meta.lds_tokens);
-    const long grid = persistent_grid(pl.units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : (pl.staged ? 512 : 1024),
+    const long grid = persistent_grid(pl.units_upper, cfg.grid_cap > 0 ? cfg.grid_cap : (pl.staged ? kStagedGridCap : 1024),
                                       reinterpret_cast<const void *>(pl.fn), kThreads, lds);
     hipLaunchKernelGGL(pl.fn, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();

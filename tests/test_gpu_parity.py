@@ -433,8 +433,9 @@ def test_shrink_stream_k(cfg, slices, rank, hidden, fused, monkeypatch):
 @pytest.mark.parametrize("fused", [False, True])
 def test_shrink_walk_boundary(n, fused):
     """The automatic choice on both sides of the stream-K threshold (1024
-    tokens: units below, stream-K from there on), with long segments (the
-    LDS-staged kernel), 192 weight rows and K not a multiple of 64."""
+    tokens: units below; from there on stream-K unless one round of whole
+    units fits on the GPU), with long segments (the LDS-staged kernel), 192
+    weight rows and K not a multiple of 64."""
     wl = workloads.random_case(360 + n, n, 1000, (64, 64, 64), 64, 4, bias=True, neg_fraction=0.05)
     print("shrink walk boundary", n, fused, flush=True)
     H.run_and_check(wl, add_inputs=True, fused=fused)
@@ -865,12 +866,13 @@ def test_prepare_fused_graph_replay():
     meta.struct.host_no_lora = None
 
 
-def test_stream_k_graph_replay():
-    """A captured lora_prepare_shrink_expand on a batch the stream-K shrink
-    serves (1500 tokens, long segments), replayed for several batches on
-    fixed buffers (one all -1, one single id, one half -1) with eager work
-    between replays: metadata, buffer and output checked against the oracle
-    after every replay, and the stream-K counters left zero."""
+def test_stream_k_graph_replay(monkeypatch):
+    """A captured lora_prepare_shrink_expand with the stream-K shrink (1500
+    tokens, long segments), replayed for several batches on fixed buffers
+    (one all -1, one single id, one half -1) with eager work between
+    replays: metadata, buffer and output checked against the oracle after
+    every replay, and the stream-K counters left zero."""
+    monkeypatch.setenv("LORA_SHRINK_SK", "2")
     sgl = H.lib()
     base = workloads.random_case(391, 1500, 712, (64, 64, 64), 64, 6, bias=True, neg_fraction=0.05)
     L = base.layers[0]
