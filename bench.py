@@ -230,6 +230,15 @@ def call_kinds(wl, li: int, with_prepare: bool):
     return (prepare_kinds(wl.mapping.numel(), wl.spec.max_loras) if with_prepare else []) + zero + ["shrink", "expand"]
 
 
+def cold_sets(call_bytes: int, set_bytes_: int) -> int:
+    """Input sets a call cycles over when it is timed on its own: enough that
+    twice the last-level cache streams between two uses of one set (at least
+    two sets; at most 64 or 16 GiB of sets)."""
+    need = 1 + math.ceil(2 * LLC_BYTES / max(call_bytes, 1))
+    cap = max(2, min(64, (16 << 30) // max(set_bytes_, 1)))
+    return max(2, min(cap, need))
+
+
 def set_bytes(wl) -> int:
     tot = wl.mapping.numel() * 4
     for L in wl.layers:
@@ -679,18 +688,20 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
     print("# %s: timed %d steps in %.4f s" % (name, steps, elapsed), file=sys.stderr, flush=True)
 
     # per-call average durations: graphs of >= 32 launches of one call kind
-    # cycling over the input sets; at least two sets, so that a call never
-    # finds the inputs of the launch before it in the last-level cache (a step
-    # streams the other calls' data in between)
+    # cycling over enough input sets that a launch finds none of its inputs
+    # in the last-level cache, as inside a step (which streams the other
+    # calls' data in between)
     PLAN.phase = "per_call"
-    if rotate == 1 and not args.eager:
-        sets.append(DeviceSet(wl, src=first))
-    pc_rotate = len(sets)
-    ncalls = max(32, pc_rotate)
+    pc_sets = {}
     reps = 2
 
-    def per_call(fn):
-        g1, s1 = capture(lambda: [fn(sets[i % pc_rotate]) for i in range(ncalls)])
+    def per_call(fn, call_bytes, key):
+        k = cold_sets(call_bytes, sb)
+        while len(sets) < k:
+            sets.append(DeviceSet(wl, src=first))
+        pc_sets[key] = k
+        ncalls = max(32, k)
+        g1, s1 = capture(lambda: [fn(sets[i % k]) for i in range(ncalls)])
         g1.replay()
         PLAN.replay(s1, 1)
         # about 20 ms of replays right before the timed ones (the first
@@ -701,14 +712,16 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
         PLAN.replay(s1, n_rep)
         return time_graph(g1, s1, n_rep) / ncalls
 
-    kern = {"prepare": per_call(lambda s: s.prepare())}
+    kern = {"prepare": per_call(lambda s: s.prepare(), ab["prepare"], "prepare")}
     for li in range(nl):
         if not wl.layers[li].spec.expand_only:
-            kern["shrink%d" % li] = per_call(lambda s: s.shrink(li))
-            kern["linear%d" % li] = per_call(lambda s: s.linear(li))
-        kern["expand%d" % li] = per_call(lambda s: s.expand(li))
+            kern["shrink%d" % li] = per_call(lambda s: s.shrink(li), ab["shrink"][li], "shrink%d" % li)
+            kern["linear%d" % li] = per_call(lambda s: s.linear(li), ab["shrink_fresh"][li] + ab["expand"][li],
+                                             "linear%d" % li)
+        kern["expand%d" % li] = per_call(lambda s: s.expand(li), ab["expand"][li], "expand%d" % li)
     if not wl.layers[0].spec.expand_only:
-        kern["preplinear0"] = per_call(lambda s: s.prepare_linear(0))
+        kern["preplinear0"] = per_call(lambda s: s.prepare_linear(0),
+                                       ab["prepare"] + ab["shrink_fresh"][0] + ab["expand"][0], "preplinear0")
     torch.cuda.synchronize()
 
     bytes_of = {"prepare": ab["prepare"]}
@@ -748,7 +761,7 @@ def run_workload(name: str, args, steps: int | None, warmup: int, sub_ms: float)
            "layers": [{"hidden": L.spec.hidden, "slices": list(L.spec.slices), "rank": L.spec.rank,
                        "scale": L.spec.scale, "bias": L.bias is not None, "expand_only": L.spec.expand_only}
                       for L in wl.layers],
-           "input_sets_rotated": rotate, "per_call_input_sets": pc_rotate, "steps": steps, "ms_per_step": round(ms_per_step, 5),
+           "input_sets_rotated": rotate, "per_call_input_sets": pc_sets, "steps": steps, "ms_per_step": round(ms_per_step, 5),
            "tokens_per_s": round(tokens_per_s, 1), "step_bytes": step_bytes,
            "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
            "step_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -809,13 +822,9 @@ def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     if wl is None:
         wl = workloads.make_workload(name)
     sb = set_bytes(wl)
-    rotate = max(1, math.ceil((1 << 30) / sb)) if sb < LLC_BYTES else 1
+    ab = algorithmic_bytes(wl)
     first = DeviceSet(wl)
-    sets = [first] + [DeviceSet(wl, src=first) for _ in range(rotate - 1)]
-    for d in sets:
-        d.prepare()
-    torch.cuda.synchronize()
-    n = max(8, rotate)
+    sets = [first]
     env = ("LORA_SHRINK_STAGED", "LORA_SHRINK_KSPLIT", "LORA_SHRINK_VARIANT", "LORA_SHRINK_SK",
            "LORA_EXPAND_TILE_TOKENS", "LORA_EXPAND_RUN", "LORA_EXPAND_SHARE")
     if grid is not None:
@@ -837,11 +846,18 @@ def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
     lines = ["# %s tilings: %s workload" % (what, name), "", "Command:", "", "    " + command, "",
              "kernel_hash: " + kernel_source_hash(), "",
              "us per launch (HIP events over about 20 ms of graph replays after about 20 ms of warm ones, "
-             "%d cold input set(s)); `auto` = the launcher's choice."
-             % rotate, ""]
+             "cycling over enough input sets that a launch finds none of its inputs in the last-level cache); "
+             "`auto` = the launcher's choice.", ""]
     for li, L in enumerate(wl.layers):
         if what == "shrink" and L.spec.expand_only:
             continue
+        rotate = cold_sets(ab["shrink"][li] if what == "shrink" else ab["expand"][li], sb)
+        while len(sets) < rotate:
+            sets.append(DeviceSet(wl, src=first))
+        for d in sets:
+            d.prepare()
+        torch.cuda.synchronize()
+        n = max(8, rotate)
         res = []
         for g in grid:
             for k in env:
@@ -868,7 +884,7 @@ def sweep(name: str, what: str, out_md: str, grid=None, wl=None) -> None:
             os.environ.pop(k, None)
         res.sort()
         auto = [u for u, lab in res if lab == "auto"][0]
-        lines += ["## layer %d (best %.2f us, auto %.2f us)" % (li, res[0][0], auto), "",
+        lines += ["## layer %d (best %.2f us, auto %.2f us; %d input sets)" % (li, res[0][0], auto, rotate), "",
                   "| tiling | us |", "|---|---|"] + ["| %s | %.2f |" % (lab, u) for u, lab in res] + [""]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")

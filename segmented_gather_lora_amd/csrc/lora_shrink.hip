@@ -901,22 +901,14 @@ ShrinkPlan plan_shrink(int n, int nslots, int rows, int hidden, const ShrinkTuni
     pl.k_chunk = chunk;
     pl.units_upper = (long)tiles_upper * pl.row_blocks * ks;
 
-    // Stream-K for staged batches of at least kSkMinTokens tokens (whose
+    // Stream-K for every staged batch of at least kSkMinTokens tokens (whose
     // library-owned area holds the part slots): its equal shares leave no CU
     // with a unit more than another, and a K split needs no float atomics
     // into a cleared buffer (the slots combine the parts).  The unit walk
-    // stays for smaller batches, and for batches whose units need no K split
-    // and all fit on the GPU at once (at most one unit per workgroup of the
-    // unit walk's grid): each workgroup then runs one whole unit, as even as
-    // the shares and with no parts to combine.  LORA_SHRINK_SK=2 forces
-    // stream-K for any staged batch that size, LORA_SHRINK_SK=1 turns it off.
+    // stays for smaller batches.  LORA_SHRINK_SK=2 forces it for any staged
+    // batch that size, LORA_SHRINK_SK=1 turns it off.
     const bool automatic = cfg.stream_k == 0 && cfg.k_splits <= 0 && cfg.variant == 0 && cfg.staged_cfg <= 0;
     bool sk_auto = automatic;
-    if (automatic && pl.staged && pl.k_splits == 1) {
-        const size_t lds = sizeof(int) * (size_t)(4 * nslots + 1);
-        const long slots = resident_grid(reinterpret_cast<const void *>(pl.fn), kThreads, lds);
-        if (pl.units_upper <= (slots < kStagedGridCap ? slots : kStagedGridCap)) sk_auto = false;
-    }
     // Long K walks over more than 128 weight rows (the large shape): the
     // 128 x 192 tile as stream-K, one workgroup per CU, reads each token row
     // once per 192 rows instead of once per 128, and its shares are long

@@ -433,9 +433,8 @@ def test_shrink_stream_k(cfg, slices, rank, hidden, fused, monkeypatch):
 @pytest.mark.parametrize("fused", [False, True])
 def test_shrink_walk_boundary(n, fused):
     """The automatic choice on both sides of the stream-K threshold (1024
-    tokens: units below; from there on stream-K unless one round of whole
-    units fits on the GPU), with long segments (the LDS-staged kernel), 192
-    weight rows and K not a multiple of 64."""
+    tokens: units below, stream-K from there on), with long segments (the
+    LDS-staged kernel), 192 weight rows and K not a multiple of 64."""
     wl = workloads.random_case(360 + n, n, 1000, (64, 64, 64), 64, 4, bias=True, neg_fraction=0.05)
     print("shrink walk boundary", n, fused, flush=True)
     H.run_and_check(wl, add_inputs=True, fused=fused)
