@@ -193,3 +193,16 @@ def test_summarize_pmc_one_launch_call(tmp_path):
     out = tmp_path / "o.json"
     bench.summarize_pmc("decode", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out), "cmd")
     assert json.load(open(out))["traffic_bytes"] == {"preplinear0": 2 * 7 * 1024}
+
+
+def test_cold_sets():
+    """Input sets a call cycles over when timed alone: enough that twice the
+    last-level cache streams between two uses of one set, within the caps."""
+    llc = bench.LLC_BYTES
+    assert bench.cold_sets(4 * llc, 10 * llc) == 2             # a call larger than the cache: two sets
+    assert bench.cold_sets(llc // 4, llc) == 9                 # 1 + 2 * 4
+    assert bench.cold_sets(1, 1 << 20) == 64                   # a tiny call: at most 64 sets
+    assert bench.cold_sets(1, 8 << 30) == 2                    # at most 16 GiB of sets, at least two
+    for cb in (1 << 20, 50 << 20, 200 << 20):
+        k = bench.cold_sets(cb, 300 << 20)
+        assert k == 2 or (k - 1) * cb >= 2 * llc or k * (300 << 20) > (16 << 30) - (300 << 20)
